@@ -1,0 +1,133 @@
+/*
+ * flux_attn.h - C ABI of the MI355X (gfx950) joint RoPE attention library.
+ *
+ * The operation.  One call computes, for every batch b and head h, the
+ * non-causal softmax attention of the whole joint token sequence
+ *
+ *     O[b,i,h,:] = sum_j softmax_j( scale * <R(pos_i) Q[b,i,h,:], R(pos_j) K[b,j,h,:]> ) V[b,j,h,:]
+ *
+ * where R(p) is the multi-axis rotary position embedding of token position
+ * p = (p0, p1, p2).  Sources:
+ *   - "Welcome FLUX.3 Image Klein in Diffusers", Architecture section
+ *     ("Two-Stage Processing"): text, noisy-image and reference tokens are
+ *     concatenated and attend jointly in the joint blocks;
+ *   - "FLUX.3 Image Klein Brings 2-Second AI Image Generation to Diffusers",
+ *     Summary: five separate-stream blocks before 28 joint blocks (the
+ *     segment-local mode below is the separate-stream attention);
+ *   - "Optimizing FLUX 3 Image Klein inference on NVIDIA Blackwell GPUs",
+ *     "How it works": rotary position embeddings, and attention with query,
+ *     key and value in FP8.
+ * Conventions where the pages are silent: scale = 1/sqrt(head_dim); RoPE pairs
+ * are adjacent elements (2j, 2j+1) inside each axis slice; head_dim is cut into
+ * three slices of widths rope_axes_dim[0..2]; pair j of a slice of width d is
+ * rotated by pos_axis * theta^(-2j/d); V is not rotated.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q, k, v, out   [batch][tokens][num_heads][head_dim]
+ *   pos_ids        [tokens][3] int32, shared by every batch entry
+ *   qkv_scale      [3][batch][num_heads] float (FP8 only: q, k, v scales)
+ *
+ * Errors.  Every function returns a status code (flux_attn_status).  No C++
+ * exception crosses this boundary.  forward() checks all arguments on the host
+ * before any device work; on error nothing is launched and a thread-local
+ * message is available from flux_attn_last_error().
+ */
+#ifndef FLUX_ATTN_H
+#define FLUX_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLUX_ATTN_ABI_VERSION 1
+
+typedef enum {
+  FLUX_ATTN_OK = 0,
+  FLUX_ATTN_INVALID_ARGUMENT = 1, /* a pointer, size or shape is wrong */
+  FLUX_ATTN_UNSUPPORTED = 2,      /* valid request this build does not run */
+  FLUX_ATTN_DEVICE_ERROR = 3,     /* a HIP runtime call failed */
+  FLUX_ATTN_OUT_OF_MEMORY = 4     /* device allocation in create() failed */
+} flux_attn_status;
+
+typedef enum {
+  FLUX_ATTN_BF16 = 0,     /* q, k, v are bfloat16 */
+  FLUX_ATTN_FP8_E4M3 = 1  /* q, k, v are OCP e4m3 ("e4m3fn") codes + per-head scales */
+} flux_attn_dtype;
+
+typedef enum {
+  FLUX_ATTN_JOINT = 0,         /* every token attends to every token */
+  FLUX_ATTN_SEGMENT_LOCAL = 1  /* tokens attend only inside their own segment */
+} flux_attn_mode;
+
+typedef struct {
+  int32_t batch;            /* >= 1 */
+  int32_t num_heads;        /* >= 1 */
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t max_tokens;       /* capacity: largest token count forward() will see */
+  int32_t max_segments;     /* capacity of the segment list, >= 1 */
+  int32_t rope_axes_dim[3]; /* even, multiples of 8, sum == head_dim */
+  float rope_theta;         /* > 0, e.g. 10000 */
+  float softmax_scale;      /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t dtype;            /* flux_attn_dtype */
+} flux_attn_config;
+
+typedef struct flux_attn_plan flux_attn_plan; /* opaque; owned by the library */
+
+/* Fills *cfg with the defaults for (batch, num_heads, head_dim, max_tokens):
+ * axes (D/4, 3D/8, 3D/8), theta 10000, scale 1/sqrt(D), bf16, 12 segments
+ * (text + image + up to 10 references).  Host only; no device call. */
+int flux_attn_default_config(flux_attn_config* cfg, int32_t batch, int32_t num_heads,
+                             int32_t head_dim, int32_t max_tokens);
+
+/* Checks a configuration without touching a device.  Host only. */
+int flux_attn_validate_config(const flux_attn_config* cfg);
+
+/* Checks the host-side arguments of a forward call against cfg without touching
+ * a device: segment list (each >= 0, sum N with 1 <= N <= max_tokens, count
+ * <= max_segments), non-null and 16-byte aligned tensors, out not overlapping
+ * q/k/v (by address range), scales present iff FP8, mode known.  Host only. */
+int flux_attn_validate_forward(const flux_attn_config* cfg, const void* q, const void* k,
+                               const void* v, const float* qkv_scale,
+                               const int32_t* segment_tokens, int32_t num_segments,
+                               const int32_t* pos_ids, const void* out, int32_t mode);
+
+/* Creates a plan on the current HIP device: validates cfg and allocates the
+ * plan's device workspace once (RoPE table of max_tokens x head_dim/2 float2,
+ * split-K/V partials, counters).  *out receives the plan, or NULL on error. */
+int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out);
+
+/* Runs joint (or segment-local) RoPE attention asynchronously on hip_stream
+ * (a hipStream_t; NULL = the null stream).  q, k, v, out, pos_ids and
+ * qkv_scale are device pointers owned by the caller and must stay valid until
+ * the stream has passed this work; segment_tokens is a host array read before
+ * the call returns.  N = sum(segment_tokens).  out is fully overwritten.
+ * A plan runs one forward at a time (its workspace is shared between calls);
+ * separate plans are independent.  Returns after launching. */
+int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const void* v,
+                      const float* qkv_scale, const int32_t* segment_tokens,
+                      int32_t num_segments, const int32_t* pos_ids, void* out,
+                      int32_t mode, void* hip_stream);
+
+/* Copies the plan's configuration into *cfg. */
+int flux_attn_get_config(const flux_attn_plan* plan, flux_attn_config* cfg);
+
+/* Frees the plan and its workspace.  No work may be pending on it.
+ * NULL is accepted and ignored. */
+int flux_attn_destroy(flux_attn_plan* plan);
+
+/* Static description of a status code. */
+const char* flux_attn_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* flux_attn_last_error(void);
+
+/* ABI version of the loaded library (FLUX_ATTN_ABI_VERSION). */
+int flux_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLUX_ATTN_H */

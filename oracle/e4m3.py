@@ -1,0 +1,33 @@
+"""OCP 8-bit floating point e4m3 ("e4m3fn") decoding (oracle; test infrastructure).
+
+Format definition (OCP 8-bit Floating Point Specification, OFP8, E4M3):
+1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds
+subnormals m/8 * 2^-6; there are no infinities; S.1111.111 is NaN, so the
+largest finite magnitude is 1.110b * 2^8 = 448.
+
+Used for the FP8 workload of "Optimizing FLUX 3 Image Klein inference on NVIDIA
+Blackwell GPUs" (section "How it works": query, key and value in FP8).
+"""
+import numpy as np
+
+
+def e4m3_decode(codes):
+    """Decode uint8 codes to fp64 values (NaN for the two NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, val)
+    return sign * val
+
+
+def e4m3_table():
+    """All 256 code values, index = code."""
+    return e4m3_decode(np.arange(256, dtype=np.uint8))
+
+
+def dequantize(codes, scales):
+    """codes [B,N,H,D] uint8, scales [B,H] -> fp64 values codes * scale per (b,h)."""
+    vals = e4m3_table()[np.asarray(codes, dtype=np.uint8)]
+    return vals * np.asarray(scales, dtype=np.float64)[:, None, :, None]
