@@ -1,0 +1,310 @@
+// bf16 joint RoPE attention for gfx950 (MI355X).
+//
+// Computes O = softmax(scale * R(q) R(k)^T) V for one (batch, head, 256-row
+// query tile) per workgroup, non-causal, over the whole joint sequence of
+// text, noisy-image and reference tokens ("Welcome FLUX.3 Image Klein in
+// Diffusers", Architecture: the joint blocks attend over the concatenated
+// streams).  Rotary embedding is applied while Q and K tiles are loaded
+// ("Optimizing FLUX 3 Image Klein inference on NVIDIA Blackwell GPUs", How it
+// works: rotary embeddings fused into the surrounding kernels).
+//
+// Work decomposition
+//   workgroup = 4 waves x 64 query rows = 256 rows; K/V streamed in 64-key
+//   tiles, double-buffered in LDS (K rotated on the way in, rows padded).
+//   S^T = K Q^T is computed so that each lane owns one query (lane % 32) and
+//   16 keys per 32-key block: the softmax row reductions are in-lane plus one
+//   exchange between the two wave halves.
+//   O^T += V^T P^T reuses the S^T accumulator registers directly as the P^T
+//   operand (rounded to bf16); V^T fragments come from row-major V in LDS
+//   through the gfx950 transpose read.
+//   Online softmax (Milakov & Gimelshein 2018) with a lazily updated running
+//   max: the reference max only moves when a row's tile max exceeds it by more
+//   than 2^8 in the exp2 domain, which keeps every p <= 256 and skips most
+//   rescales of the output accumulators; the result is the same softmax.
+//
+// Layouts: q, k, v, o [B][N][H][D] bf16; rope [N][D/2] float2 (cos, sin).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace flux {
+
+template <int D>
+struct Bf16Cfg {
+  static constexpr int BM = 256;           // query rows per workgroup
+  static constexpr int BN = 64;            // keys per K/V tile
+  static constexpr int NT = 256;           // threads per workgroup
+  static constexpr int KSTEPS = D / 16;    // 16-wide d steps of Q K^T
+  static constexpr int DB = D / 32;        // 32-wide d blocks of O
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int RPP = NT / CPR;     // rows staged per pass
+  static constexpr int NPASS = BN / RPP;   // staging passes per tile
+  static constexpr int KTILEB = BN * (2 * D + 16);  // bytes per K tile in LDS
+  static constexpr int VTILEB = BN * (2 * D + 64);  // bytes per V tile in LDS
+};
+
+// LDS rows are padded instead of swizzled so that every fragment read is one
+// per-lane base address plus a compile-time offset.
+//   K rows: 2D + 16 bytes.  A 16-lane phase of the b128 fragment read touches
+//   16 distinct rows at one column; the 16-byte skew per row puts them in 16
+//   different 16-byte bank groups.
+//   V rows: 2D + 64 bytes.  A 32-lane phase of the transpose read touches 4
+//   consecutive rows x 64 bytes; the 64-byte skew makes those 256 bytes
+//   cover every bank once.
+template <int D> struct LdsRows {
+  static constexpr int K = 2 * D + 16;
+  static constexpr int V = 2 * D + 64;
+};
+
+template <int D>
+__device__ __forceinline__ int k_off(int r, int c) { return r * LdsRows<D>::K + (c << 4); }
+
+template <int D>
+__device__ __forceinline__ int v_off(int r, int c) { return r * LdsRows<D>::V + (c << 4); }
+
+// Key-row permutation for the S^T MFMA: swapping bits 2 and 3 of the MFMA row
+// makes accumulator element e of lane l hold key 16(e/8) + 8(l/32) + e%8 of its
+// 32-key block, i.e. 8 consecutive keys per P^T fragment.
+__device__ __forceinline__ int krow_perm(int r) {
+  return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Rotate the 4 adjacent bf16 pairs of one 16-byte chunk by (cos, sin).
+__device__ __forceinline__ u32x4 rope_chunk(u32x4 x, f32x4 cs01, f32x4 cs23) {
+  u32x4 y;
+  float c[4] = {cs01[0], cs01[2], cs23[0], cs23[2]};
+  float s[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x0 = bf16lo(x[i]), x1 = bf16hi(x[i]);
+    y[i] = pack_bf16(x0 * c[i] - x1 * s[i], x0 * s[i] + x1 * c[i]);
+  }
+  return y;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_bf16_kernel(AttnArgs a) {
+  using C = Bf16Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char ksm[2][C::KTILEB];
+  __shared__ __attribute__((aligned(16))) char vsm[2][C::VTILEB];
+
+  const int N = a.n_tokens, H = a.heads;
+  const int tile = xcd_tile_order(blockIdx.x, gridDim.x);
+  const int qt = tile % a.q_tiles;
+  const int bh = tile / a.q_tiles;
+  const int h = bh % H, b = bh / H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const size_t tok_stride = (size_t)H * D;  // elements between consecutive tokens
+  const uint16_t* qbase = a.q + (size_t)b * N * tok_stride + (size_t)h * D;
+  const uint16_t* kbase = a.k + (size_t)b * N * tok_stride + (size_t)h * D;
+  const uint16_t* vbase = a.v + (size_t)b * N * tok_stride + (size_t)h * D;
+  const float c = a.c;
+
+  // ---- Q fragments (B operand of S^T = K Q^T), rotated, held in registers.
+  bf16x8 qf[2][C::KSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qt * C::BM + wave * 64 + qb * 32 + l32;
+    const bool ok = row < N;
+#pragma unroll
+    for (int t = 0; t < C::KSTEPS; ++t) {
+      const int d0 = 16 * t + 8 * g;
+      u32x4 x = {0, 0, 0, 0};
+      f32x4 cs01 = {1.f, 0.f, 1.f, 0.f}, cs23 = {1.f, 0.f, 1.f, 0.f};
+      if (ok) {
+        x = global_load_b128(qbase + (size_t)row * tok_stride + d0);
+        const f32x4* rp = (const f32x4*)(a.rope + (size_t)row * (D / 2) + d0 / 2);
+        cs01 = rp[0];
+        cs23 = rp[1];
+      }
+      qf[qb][t] = __builtin_bit_cast(bf16x8, rope_chunk(x, cs01, cs23));
+    }
+  }
+
+  // ---- staging of one K/V tile: global -> registers (K rotated) -> LDS.
+  const int st_chunk = tid % C::CPR;
+  const int st_row0 = tid / C::CPR;
+  u32x4 kraw[C::NPASS], vraw[C::NPASS];
+  f32x4 kcs[C::NPASS][2];
+  auto stage_load = [&](int kt0) {
+#pragma unroll
+    for (int p = 0; p < C::NPASS; ++p) {
+      const int key = kt0 + st_row0 + p * C::RPP;
+      kraw[p] = (u32x4){0, 0, 0, 0};
+      vraw[p] = (u32x4){0, 0, 0, 0};
+      kcs[p][0] = (f32x4){1.f, 0.f, 1.f, 0.f};
+      kcs[p][1] = (f32x4){1.f, 0.f, 1.f, 0.f};
+      if (key < N) {
+        kraw[p] = global_load_b128(kbase + (size_t)key * tok_stride + st_chunk * 8);
+        vraw[p] = global_load_b128(vbase + (size_t)key * tok_stride + st_chunk * 8);
+        const f32x4* rp = (const f32x4*)(a.rope + (size_t)key * (D / 2) + st_chunk * 4);
+        kcs[p][0] = rp[0];
+        kcs[p][1] = rp[1];
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+    FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
+    FLUX_LDS char* vl = (FLUX_LDS char*)vsm[buf];
+#pragma unroll
+    for (int p = 0; p < C::NPASS; ++p) {
+      const int r = st_row0 + p * C::RPP;
+      lds_write_b128(kl + k_off<D>(r, st_chunk), rope_chunk(kraw[p], kcs[p][0], kcs[p][1]));
+      lds_write_b128(vl + v_off<D>(r, st_chunk), vraw[p]);
+    }
+  };
+
+  f32x16 o[2][C::DB];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) o[qb][db] = (f32x16){};
+  float m_ref[2] = {-INFINITY, -INFINITY};
+  float lsum[2] = {0.f, 0.f};
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  const int n_tiles = (N + C::BN - 1) / C::BN;
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < n_tiles) stage_load((j + 1) * C::BN);
+    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[buf];
+    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[buf];
+
+    // ---- S^T = K Q^T for 2 key blocks x 2 query blocks.
+    f32x16 s[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb][0] = (f32x16){};
+      s[kb][1] = (f32x16){};
+      const int krow = 32 * kb + krow_perm(l32);
+#pragma unroll
+      for (int t = 0; t < C::KSTEPS; ++t) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, lds_read_b128(kl + k_off<D>(krow, 2 * t + g)));
+        s[kb][0] = mfma_bf16(kf, qf[0][t], s[kb][0]);
+        s[kb][1] = mfma_bf16(kf, qf[1][t], s[kb][1]);
+      }
+    }
+
+    // ---- mask keys past the end (last tile only).
+    const int kt0 = j * C::BN;
+    if (kt0 + C::BN > N) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt0 + 32 * kb + 16 * (e >> 3) + 8 * g + (e & 7);
+          if (key >= N) {
+            s[kb][0][e] = -INFINITY;
+            s[kb][1][e] = -INFINITY;
+          }
+        }
+    }
+
+    // ---- online softmax: tile row max, lazy rescale of the running state.
+    float mref[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mt = s[0][qb][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[0][qb][e]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[1][qb][e]);
+      mt = fmaxf(mt, swap_halves(mt));
+      const float ms = mt * c;
+      const bool need = ms > m_ref[qb] + 8.0f;
+      if (__ballot(need) != 0) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[qb] - ms) : 1.0f;
+        m_ref[qb] = need ? ms : m_ref[qb];
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) o[qb][db] *= alpha;
+      }
+      mref[qb] = m_ref[qb];
+    }
+
+    // ---- P = exp2(S c - m) as bf16 P^T fragments, then O^T += V^T P^T, one
+    // 16-key slice at a time.
+    const int grp = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 pf[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * hh + 2 * i], c, -mref[qb]));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * hh + 2 * i + 1], c, -mref[qb]));
+            // Row sums over the bf16-rounded P (the values the PV product uses).
+            // The dot operand is built as a bf16x2 directly: passing a bit-cast
+            // element of w here made the compiler feed the same register to
+            // every dot instruction.
+            bf16x2 pp;
+            pp[0] = (__bf16)p0;
+            pp[1] = (__bf16)p1;
+            w[i] = __builtin_bit_cast(uint32_t, pp);
+            lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum[qb], false);
+          }
+          pf[qb] = __builtin_bit_cast(bf16x8, w);
+        }
+        const int krow0 = 32 * kb + 16 * hh + 8 * (grp >> 1) + (li >> 2);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int d = 32 * db + 16 * (grp & 1) + 4 * (li & 3);
+          const int cb = (d & 7) * 2;
+          const u32x2 lo = lds_read_tr16(vl + v_off<D>(krow0, d >> 3) + cb);
+          const u32x2 hi = lds_read_tr16(vl + v_off<D>(krow0 + 4, d >> 3) + cb);
+          const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+          o[0][db] = mfma_bf16(vf, pf[0], o[0][db]);
+          o[1][db] = mfma_bf16(vf, pf[1], o[1][db]);
+        }
+      }
+
+    if (j + 1 < n_tiles) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O^T / l, bf16, stored row-major.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qt * C::BM + wave * 64 + qb * 32 + l32;
+    const float inv = 1.0f / (lsum[qb] + swap_halves(lsum[qb]));
+    if (row < N) {
+      uint16_t* orow = a.o + (size_t)b * N * tok_stride + (size_t)row * tok_stride + (size_t)h * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa) {
+          const int d = 32 * db + 8 * aa + 4 * g;
+          u32x2 w;
+          w[0] = pack_bf16(o[qb][db][4 * aa + 0] * inv, o[qb][db][4 * aa + 1] * inv);
+          w[1] = pack_bf16(o[qb][db][4 * aa + 2] * inv, o[qb][db][4 * aa + 3] * inv);
+          *(u32x2*)(orow + d) = w;
+        }
+    }
+  }
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t stream) {
+  const int q_tiles = (a.n_tokens + 255) / 256;
+  const int grid = q_tiles * a.heads * a.batch;
+  AttnArgs args = a;
+  args.q_tiles = q_tiles;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, args);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, args);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace flux

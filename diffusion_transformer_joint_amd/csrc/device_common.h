@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, MFMA
+// wrappers, bf16 packing, LDS transpose reads and XCD-aware tile order.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flux {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FLUX_LDS __attribute__((address_space(3)))
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%32][8(l/32)..+8]
+// and B[8(l/32)..+8][l%32]; result element e of lane l is
+// C[8(e/4) + 4(l/32) + e%4][l%32].
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x64 fp8(e4m3) x fp8(e4m3) MFMA, fp32 accumulate.  Lane l supplies 32
+// codes of row l%32 of A and of column l%32 of B; the k split between lanes l
+// and l+32 only has to agree between A and B.
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bf16 (nearest even) and pack: a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Inside each group of 16
+// lanes, lane i receives half-word (i % 4) of the 8 bytes addressed by lanes
+// 4e + i/4, e = 0..3, as its element e.
+__device__ __forceinline__ u32x2 lds_read_tr16(const FLUX_LDS void* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FLUX_LDS i16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128(const FLUX_LDS void* p) {
+  return *(const FLUX_LDS u32x4*)p;
+}
+
+__device__ __forceinline__ void lds_write_b128(FLUX_LDS void* p, u32x4 v) {
+  *(FLUX_LDS u32x4*)p = v;
+}
+
+__device__ __forceinline__ u32x4 global_load_b128(const void* p) {
+  return *(const u32x4*)p;
+}
+
+// Value of lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32);
+}
+
+// Tiles are dispatched round-robin over the 8 XCDs (block i runs on XCD i % 8).
+// Remap so that each XCD receives a contiguous range of logical tiles: tiles of
+// one head then share that XCD's L2.  A bijection on [0, total).
+__device__ __forceinline__ int xcd_tile_order(int i, int total) {
+  const int nx = 8;
+  int per = total / nx, rem = total % nx;
+  int x = i % nx, k = i / nx;
+  return x * per + (x < rem ? x : rem) + k;
+}
+
+}  // namespace flux

@@ -1,0 +1,275 @@
+// Host side of the joint RoPE attention library: the C ABI declared in
+// include/flux_attn.h (argument validation, plan lifetime, launches).
+//
+// Validation runs entirely on the host before any HIP call, so every error
+// path can be exercised without a GPU.
+#include "flux_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FLUX_ATTN_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorOutOfMemory ? FLUX_ATTN_OUT_OF_MEMORY : FLUX_ATTN_DEVICE_ERROR,
+              "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_bytes(int dtype) { return dtype == FLUX_ATTN_FP8_E4M3 ? 1 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bn && y < x + an;
+}
+
+}  // namespace
+
+struct flux_attn_plan {
+  flux_attn_config cfg;
+  int device = -1;
+  float2* rope_table = nullptr;  // [max_tokens][head_dim/2]
+  double* freq = nullptr;        // [head_dim/2]
+};
+
+namespace {
+
+// Registry of live plans, so a destroyed or foreign pointer is rejected
+// without being dereferenced.
+std::mutex g_plans_mu;
+std::unordered_set<const flux_attn_plan*> g_plans;
+
+bool plan_live(const flux_attn_plan* p) {
+  std::lock_guard<std::mutex> lk(g_plans_mu);
+  return p && g_plans.count(p) != 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flux_attn_abi_version(void) { return FLUX_ATTN_ABI_VERSION; }
+
+const char* flux_attn_status_string(int status) {
+  switch (status) {
+    case FLUX_ATTN_OK: return "ok";
+    case FLUX_ATTN_INVALID_ARGUMENT: return "invalid argument";
+    case FLUX_ATTN_UNSUPPORTED: return "unsupported";
+    case FLUX_ATTN_DEVICE_ERROR: return "device error";
+    case FLUX_ATTN_OUT_OF_MEMORY: return "out of device memory";
+    default: return "unknown status";
+  }
+}
+
+const char* flux_attn_last_error(void) { return g_last_error.c_str(); }
+
+int flux_attn_default_config(flux_attn_config* cfg, int32_t batch, int32_t num_heads, int32_t head_dim,
+                             int32_t max_tokens) {
+  if (!cfg) return fail(FLUX_ATTN_INVALID_ARGUMENT, "cfg is NULL");
+  std::memset(cfg, 0, sizeof *cfg);
+  cfg->batch = batch;
+  cfg->num_heads = num_heads;
+  cfg->head_dim = head_dim;
+  cfg->max_tokens = max_tokens;
+  cfg->max_segments = 12;
+  cfg->rope_axes_dim[0] = head_dim / 4;
+  cfg->rope_axes_dim[1] = 3 * head_dim / 8;
+  cfg->rope_axes_dim[2] = 3 * head_dim / 8;
+  cfg->rope_theta = 10000.0f;
+  cfg->softmax_scale = 0.0f;
+  cfg->dtype = FLUX_ATTN_BF16;
+  return ok();
+}
+
+int flux_attn_validate_config(const flux_attn_config* c) {
+  if (!c) return fail(FLUX_ATTN_INVALID_ARGUMENT, "config is NULL");
+  if (c->batch < 1) return fail(FLUX_ATTN_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", c->batch);
+  if (c->num_heads < 1) return fail(FLUX_ATTN_INVALID_ARGUMENT, "num_heads must be >= 1 (got %d)", c->num_heads);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(FLUX_ATTN_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
+  if (c->max_tokens < 1) return fail(FLUX_ATTN_INVALID_ARGUMENT, "max_tokens must be >= 1 (got %d)", c->max_tokens);
+  if (c->max_segments < 1)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "max_segments must be >= 1 (got %d)", c->max_segments);
+  int sum = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int d = c->rope_axes_dim[a];
+    if (d < 0 || d % 8)
+      return fail(FLUX_ATTN_INVALID_ARGUMENT, "rope_axes_dim[%d] = %d must be a non-negative multiple of 8", a, d);
+    sum += d;
+  }
+  if (sum != c->head_dim)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "rope_axes_dim sums to %d, head_dim is %d", sum, c->head_dim);
+  if (!(c->rope_theta > 0.0f) || !std::isfinite(c->rope_theta))
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "rope_theta must be finite and > 0");
+  if (!std::isfinite(c->softmax_scale)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (c->dtype != FLUX_ATTN_BF16 && c->dtype != FLUX_ATTN_FP8_E4M3)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "unknown dtype %d", c->dtype);
+  // Offsets inside one [B][N][H][D] tensor are formed in 64-bit; the token count
+  // must still index a 32-bit grid.
+  const double elems = (double)c->batch * c->max_tokens * c->num_heads * c->head_dim;
+  if (elems > 9.0e15) return fail(FLUX_ATTN_INVALID_ARGUMENT, "tensor too large");
+  return ok();
+}
+
+int flux_attn_validate_forward(const flux_attn_config* c, const void* q, const void* k, const void* v,
+                               const float* qkv_scale, const int32_t* segment_tokens, int32_t num_segments,
+                               const int32_t* pos_ids, const void* out, int32_t mode) {
+  int st = flux_attn_validate_config(c);
+  if (st) return st;
+  if (mode != FLUX_ATTN_JOINT && mode != FLUX_ATTN_SEGMENT_LOCAL)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "unknown mode %d", mode);
+  if (!segment_tokens) return fail(FLUX_ATTN_INVALID_ARGUMENT, "segment_tokens is NULL");
+  if (num_segments < 1 || num_segments > c->max_segments)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "num_segments = %d outside [1, %d]", num_segments, c->max_segments);
+  long long n = 0;
+  for (int i = 0; i < num_segments; ++i) {
+    if (segment_tokens[i] < 0)
+      return fail(FLUX_ATTN_INVALID_ARGUMENT, "segment_tokens[%d] = %d is negative", i, segment_tokens[i]);
+    n += segment_tokens[i];
+  }
+  if (n < 1) return fail(FLUX_ATTN_INVALID_ARGUMENT, "total token count is 0");
+  if (n > c->max_tokens)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "total token count %lld exceeds max_tokens %d", n, c->max_tokens);
+  if (!q || !k || !v || !out || !pos_ids) return fail(FLUX_ATTN_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(pos_ids) & 3u) != 0)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "pos_ids must be 4-byte aligned");
+  const bool fp8 = c->dtype == FLUX_ATTN_FP8_E4M3;
+  if (fp8 && !qkv_scale) return fail(FLUX_ATTN_INVALID_ARGUMENT, "FP8 inputs need qkv_scale");
+  if (!fp8 && qkv_scale) return fail(FLUX_ATTN_INVALID_ARGUMENT, "qkv_scale is only used with FP8 inputs");
+  const size_t in_bytes = (size_t)c->batch * (size_t)n * c->num_heads * c->head_dim * elem_bytes(c->dtype);
+  const size_t out_bytes = (size_t)c->batch * (size_t)n * c->num_heads * c->head_dim * 2;
+  if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
+      overlaps(out, out_bytes, v, in_bytes))
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "out overlaps q, k or v");
+  return ok();
+}
+
+int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
+  if (!out) return fail(FLUX_ATTN_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  int st = flux_attn_validate_config(cfg);
+  if (st) return st;
+  auto* p = new (std::nothrow) flux_attn_plan();
+  if (!p) return fail(FLUX_ATTN_OUT_OF_MEMORY, "host allocation failed");
+  p->cfg = *cfg;
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipGetDevice");
+  }
+  const int half = cfg->head_dim / 2;
+  std::vector<double> freq(half);
+  int j0 = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int d = cfg->rope_axes_dim[a];
+    for (int j = 0; j < d / 2; ++j) freq[j0 + j] = std::pow((double)cfg->rope_theta, -2.0 * j / d);
+    j0 += d / 2;
+  }
+  e = hipMalloc(&p->rope_table, (size_t)cfg->max_tokens * half * sizeof(float2));
+  if (e == hipSuccess) e = hipMalloc(&p->freq, half * sizeof(double));
+  if (e == hipSuccess) e = hipMemcpy(p->freq, freq.data(), half * sizeof(double), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(p->rope_table);
+    (void)hipFree(p->freq);
+    delete p;
+    return hip_fail(e, "plan workspace");
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_plans_mu);
+    g_plans.insert(p);
+  }
+  *out = p;
+  return ok();
+}
+
+int flux_attn_get_config(const flux_attn_plan* plan, flux_attn_config* cfg) {
+  if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
+  if (!cfg) return fail(FLUX_ATTN_INVALID_ARGUMENT, "cfg is NULL");
+  *cfg = plan->cfg;
+  return ok();
+}
+
+int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const void* v, const float* qkv_scale,
+                      const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
+                      int32_t mode, void* hip_stream) {
+  if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
+  const flux_attn_config& c = plan->cfg;
+  int st = flux_attn_validate_forward(&c, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out, mode);
+  if (st) return st;
+  int n = 0;
+  for (int i = 0; i < num_segments; ++i) n += segment_tokens[i];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan was created on device %d, current device is %d", plan->device, dev);
+  if (mode != FLUX_ATTN_JOINT) return fail(FLUX_ATTN_UNSUPPORTED, "segment-local mode is not built yet");
+  if (c.dtype == FLUX_ATTN_FP8_E4M3) return fail(FLUX_ATTN_UNSUPPORTED, "FP8 kernel is not built yet");
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  e = flux::launch_rope_table(pos_ids, plan->freq, plan->rope_table, n, c.head_dim, c.rope_axes_dim[0],
+                              c.rope_axes_dim[1], stream);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  const float scale = c.softmax_scale > 0.0f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
+  const float log2e = 1.4426950408889634f;
+  flux::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(out);
+  a.rope = plan->rope_table;
+  a.n_tokens = n;
+  a.heads = c.num_heads;
+  a.batch = c.batch;
+  a.c = scale * log2e;
+  e = flux::launch_attn_bf16(a, c.head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+int flux_attn_destroy(flux_attn_plan* plan) {
+  if (!plan) return ok();
+  {
+    std::lock_guard<std::mutex> lk(g_plans_mu);
+    if (!g_plans.erase(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is not live (destroyed or foreign)");
+  }
+  hipError_t e1 = hipFree(plan->rope_table);
+  hipError_t e2 = hipFree(plan->freq);
+  delete plan;
+  if (e1 != hipSuccess) return hip_fail(e1, "hipFree");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
+  return ok();
+}
+
+}  // extern "C"

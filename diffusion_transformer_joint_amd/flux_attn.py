@@ -1,0 +1,201 @@
+"""Python binding of the joint RoPE attention library (libflux_attn.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/flux_attn.h``.  PyTorch supplies device
+memory and the stream.  There is no CPU fallback: if the shared library is
+missing, loading raises ``FluxAttnError``.
+
+    plan = Plan(batch=1, num_heads=24, head_dim=128, max_tokens=8704)
+    out = plan.forward(q, k, v, segment_tokens=[512, 4096, 4096], pos_ids=pos)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflux_attn.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "flux_attn.h")
+
+OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR, OUT_OF_MEMORY = 0, 1, 2, 3, 4
+BF16, FP8_E4M3 = 0, 1
+JOINT, SEGMENT_LOCAL = 0, 1
+_MODES = {"joint": JOINT, "segment_local": SEGMENT_LOCAL}
+
+
+class FluxAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32),
+        ("max_segments", ctypes.c_int32),
+        ("rope_axes_dim", ctypes.c_int32 * 3),
+        ("rope_theta", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_vp, _i32, _i32p, _fp = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libflux_attn.so (built by ``python -m diffusion_transformer_joint_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FluxAttnError(DEVICE_ERROR, f"{p} is missing: build it with "
+                            "`python -m diffusion_transformer_joint_amd.build`")
+    lib = ctypes.CDLL(p)
+    cp = ctypes.POINTER(Config)
+    sig = {
+        "flux_attn_default_config": ([cp, _i32, _i32, _i32, _i32], ctypes.c_int),
+        "flux_attn_validate_config": ([cp], ctypes.c_int),
+        "flux_attn_validate_forward": ([cp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _i32], ctypes.c_int),
+        "flux_attn_create": ([cp, ctypes.POINTER(_vp)], ctypes.c_int),
+        "flux_attn_forward": ([_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _i32, _vp], ctypes.c_int),
+        "flux_attn_get_config": ([_vp, cp], ctypes.c_int),
+        "flux_attn_destroy": ([_vp], ctypes.c_int),
+        "flux_attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "flux_attn_last_error": ([], ctypes.c_char_p),
+        "flux_attn_abi_version": ([], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def header_functions(header: str = HEADER_PATH) -> list:
+    """Names of the functions include/flux_attn.h declares."""
+    text = open(header).read()
+    return sorted(set(re.findall(r"\b(flux_attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def last_error() -> str:
+    return load_library().flux_attn_last_error().decode()
+
+
+def check(status: int, what: str = "flux_attn") -> None:
+    if status != OK:
+        lib = load_library()
+        raise FluxAttnError(status, f"{what}: {lib.flux_attn_status_string(status).decode()}: "
+                            f"{lib.flux_attn_last_error().decode()}")
+
+
+def default_config(batch: int, num_heads: int, head_dim: int, max_tokens: int, dtype: str = "bf16",
+                   rope_axes_dim: Optional[Sequence[int]] = None, rope_theta: float = 10000.0,
+                   softmax_scale: float = 0.0, max_segments: int = 12) -> Config:
+    lib = load_library()
+    cfg = Config()
+    check(lib.flux_attn_default_config(ctypes.byref(cfg), batch, num_heads, head_dim, max_tokens),
+          "default_config")
+    if rope_axes_dim is not None:
+        for i in range(3):
+            cfg.rope_axes_dim[i] = int(rope_axes_dim[i])
+    cfg.rope_theta = rope_theta
+    cfg.softmax_scale = softmax_scale
+    cfg.max_segments = max_segments
+    cfg.dtype = {"bf16": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3}[dtype]
+    return cfg
+
+
+def _i32_array(values: Sequence[int]):
+    arr = (ctypes.c_int32 * len(values))(*[int(v) for v in values])
+    return arr
+
+
+class Plan:
+    """A plan for one configuration; owns the library's device workspace."""
+
+    def __init__(self, batch: int, num_heads: int, head_dim: int, max_tokens: int, dtype: str = "bf16",
+                 rope_axes_dim: Optional[Sequence[int]] = None, rope_theta: float = 10000.0,
+                 softmax_scale: float = 0.0, max_segments: int = 12):
+        self._lib = load_library()
+        self.config = default_config(batch, num_heads, head_dim, max_tokens, dtype, rope_axes_dim,
+                                     rope_theta, softmax_scale, max_segments)
+        handle = ctypes.c_void_p()
+        check(self._lib.flux_attn_create(ctypes.byref(self.config), ctypes.byref(handle)), "create")
+        self._handle = handle
+
+    @property
+    def fp8(self) -> bool:
+        return self.config.dtype == FP8_E4M3
+
+    def forward(self, q, k, v, segment_tokens: Sequence[int], pos_ids, out=None, scales=None,
+                mode: str = "joint", stream=None):
+        """Attention over torch device tensors on ``stream`` (default: current stream).
+
+        q, k, v: [B, N, H, D] contiguous bf16 (or uint8 / float8_e4m3fn codes for an
+        FP8 plan); pos_ids: [N, 3] int32; scales: [3, B, H] float32 (FP8 only);
+        out: optional [B, N, H, D] bf16 destination.  Returns out.
+        """
+        import torch
+
+        if self._handle is None:
+            raise FluxAttnError(INVALID_ARGUMENT, "plan is closed")
+        for name, t in (("q", q), ("k", k), ("v", v), ("pos_ids", pos_ids)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise FluxAttnError(INVALID_ARGUMENT, f"{name} must be a contiguous device tensor")
+        want = (torch.uint8, torch.float8_e4m3fn) if self.fp8 else (torch.bfloat16,)
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if t.dtype not in want:
+                raise FluxAttnError(INVALID_ARGUMENT, f"{name} has dtype {t.dtype}, expected {want}")
+        if pos_ids.dtype != torch.int32:
+            raise FluxAttnError(INVALID_ARGUMENT, "pos_ids must be int32")
+        n = int(sum(segment_tokens))
+        c = self.config
+        shape = (c.batch, n, c.num_heads, c.head_dim)
+        if tuple(q.shape) != shape or tuple(k.shape) != shape or tuple(v.shape) != shape:
+            raise FluxAttnError(INVALID_ARGUMENT, f"q/k/v must have shape {shape}")
+        if tuple(pos_ids.shape) != (n, 3):
+            raise FluxAttnError(INVALID_ARGUMENT, f"pos_ids must have shape {(n, 3)}")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
+        elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+            raise FluxAttnError(INVALID_ARGUMENT, f"out must be a contiguous bf16 tensor of shape {shape}")
+        sp = None
+        if scales is not None:
+            if tuple(scales.shape) != (3, c.batch, c.num_heads) or scales.dtype != torch.float32 \
+                    or not scales.is_cuda or not scales.is_contiguous():
+                raise FluxAttnError(INVALID_ARGUMENT, "scales must be a contiguous float32 [3, B, H] device tensor")
+            sp = scales.data_ptr()
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        segs = _i32_array(segment_tokens)
+        check(self._lib.flux_attn_forward(self._handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), sp,
+                                          segs, len(segment_tokens), pos_ids.data_ptr(), out.data_ptr(),
+                                          _MODES[mode], stream.cuda_stream), "forward")
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None:
+            h, self._handle = self._handle, None
+            check(self._lib.flux_attn_destroy(h), "destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
