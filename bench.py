@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark: joint RoPE attention on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+the RoPE angle table plus the joint attention kernel (RoPE fused into its Q/K
+loads, online softmax, bf16 MFMA), through the C ABI.  The timed workload is the
+1024^2 single-reference edit call: 512 text + 4,096 image + 4,096 reference
+tokens (8,704), 24 heads, head_dim 128, bf16 Q/K/V ~ N(0, 0.25).  Inputs are
+resident in HBM before timing starts.  The 4,608-token text-to-image call (and,
+with --all, the 25,088-token and FP8 66,048-token calls) are reported as extra
+fields of the same JSON line.
+
+Rank 0 prints one JSON line.  Only one GPU is supported: the path shards over
+heads with no communication inside the kernel, and this build measures one
+GPU's share.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "joint-attention TFLOP/s and % MFMA peak at 4,608 and 8,704 tokens, 1 GPU"
+BF16_PEAK = 2516.6   # TFLOP/s, MI355X dense bf16 MFMA (published)
+FP8_PEAK = 5033.2    # TFLOP/s, MI355X dense fp8 MFMA (published)
+HBM_PEAK = 8000.0    # GB/s
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "attn_bf16": os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc", "attn_bf16.hip"),
+    "attn_fp8": os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc", "attn_fp8.hip"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kernel):
+    p = KERNEL_SOURCES[kernel]
+    if not os.path.exists(p):
+        return None
+    h = hashlib.sha256()
+    for f in (p, os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc", "device_common.h")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it matches the source."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != source_sha(kernel):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def measure(workload, steps, warmup):
+    import torch
+    from diffusion_transformer_joint_amd import inputs as I
+    from diffusion_transformer_joint_amd.flux_attn import Plan
+
+    w = I.WORKLOADS[workload]
+    inp = I.make_inputs(w)
+    dev = torch.device("cuda:0")
+    if inp.scales is None:
+        cv = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+        sc = None
+    else:
+        cv = lambda a: torch.from_numpy(a).to(dev)
+        sc = torch.from_numpy(inp.scales).to(dev)
+    q, k, v = cv(inp.q), cv(inp.k), cv(inp.v)
+    pos = torch.from_numpy(inp.pos).to(dev)
+    out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    plan = Plan(w.batch, w.heads, w.head_dim, w.tokens, dtype="fp8" if w.fp8 else "bf16")
+    segs = w.segment_tokens
+    for _ in range(warmup):
+        plan.forward(q, k, v, segs, pos, out=out, scales=sc)
+    torch.cuda.synchronize()
+    plan.timing_enable(steps)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        plan.forward(q, k, v, segs, pos, out=out, scales=sc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = plan.timing_read()
+    plan.close()
+    step_ms = e0.elapsed_time(e1) / steps
+    flops = w.flops()
+    kavg = sum(kernel_ms) / len(kernel_ms)
+    return {
+        "workload": w.name, "tokens": w.tokens, "heads": w.heads, "head_dim": w.head_dim, "batch": w.batch,
+        "dtype": "fp8_e4m3" if w.fp8 else "bf16", "flops": flops,
+        "ms_per_step": step_ms, "wall_ms_per_step": (t1 - t0) * 1e3 / steps,
+        "kernel_ms_avg": kavg, "kernel_ms_min": min(kernel_ms),
+        "tflops": flops / (step_ms * 1e-3) / 1e12, "kernel_tflops": flops / (kavg * 1e-3) / 1e12,
+    }
+
+
+def cpu_baseline(workload, rows_count):
+    """The fp64 oracle, as it stands, on a bounded sample of query rows."""
+    import numpy as np
+    import oracle
+    from diffusion_transformer_joint_amd import inputs as I
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    w = I.WORKLOADS[workload]
+    inp = I.make_inputs(w)
+    q, k, v = oracle.inputs_to_fp64(inp)
+    rows = np.linspace(0, w.tokens - 1, rows_count).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.joint_rope_attention_rows(q, k, v, inp.pos, w.axes_dim, rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.batch * w.heads * len(rows) * w.tokens * w.head_dim
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} of {w.tokens} query rows, all {w.heads} heads, full K/V "
+                      f"(RoPE of all keys included), {workload}; {dt:.1f} s"}
+
+
+def calibrate_copy(mb):
+    """Plain device copy of a known size, for scaling HBM counters."""
+    import torch
+    n = mb * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="edit1024")
+    ap.add_argument("--all", action="store_true", help="also time the 25,088-token and FP8 workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=8704)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="only run a plain copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: joint attention shards over heads with no communication "
+              "inside the kernel, and this build times one GPU's share; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy_mb:
+        calibrate_copy(args.calibrate_copy_mb)
+        return
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    main_run = measure(args.workload, args.steps, args.warmup)
+    log(f"{args.workload}: {main_run['kernel_tflops']:.1f} TFLOP/s kernel, {main_run['ms_per_step']:.3f} ms/step")
+    extra = []
+    others = ["t2i1024"] + (["gen2048r2"] if args.all else [])
+    for name in others:
+        if name == args.workload:
+            continue
+        r = measure(name, max(5, args.steps // 2), max(2, args.warmup // 2))
+        r["frac_bf16_peak"] = r["kernel_tflops"] / BF16_PEAK
+        extra.append(r)
+        log(f"{name}: {r['kernel_tflops']:.1f} TFLOP/s kernel")
+
+    kernel = "attn_bf16"
+    traffic = recorded_traffic(kernel, args.workload)
+    achieved = main_run["kernel_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_run["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_run["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: 1024^2 single-reference edit call, 512 text + 4096 image + "
+                               f"4096 reference tokens", "batch": main_run["batch"], "seq_len": main_run["tokens"],
+                   "heads": main_run["heads"], "head_dim": main_run["head_dim"], "parallelism": "none (1 GPU)"},
+        "frac_bf16_peak": round(main_run["tflops"] / BF16_PEAK, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK, 4), "traffic": traffic,
+                     "kernel": "attn_fwd_bf16_kernel<128>", "kernel_ms_avg": round(main_run["kernel_ms_avg"], 4),
+                     "flops_per_launch": main_run["flops"]},
+        "extra": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in extra],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

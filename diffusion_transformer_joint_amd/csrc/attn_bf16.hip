@@ -9,8 +9,9 @@
 // works: rotary embeddings fused into the surrounding kernels).
 //
 // Work decomposition
-//   workgroup = 4 waves x 64 query rows = 256 rows; K/V streamed in 64-key
-//   tiles, double-buffered in LDS (K rotated on the way in, rows padded).
+//   workgroup = 8 waves x 32 query rows = 256 rows (two waves per SIMD, so one
+//   wave's softmax can run while the other issues MFMAs); K/V streamed in
+//   64-key tiles, double-buffered in LDS (K rotated on the way in, rows padded).
 //   S^T = K Q^T is computed so that each lane owns one query (lane % 32) and
 //   16 keys per 32-key block: the softmax row reductions are in-lane plus one
 //   exchange between the two wave halves.
@@ -26,13 +27,15 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace flux {
 
 template <int D>
 struct Bf16Cfg {
   static constexpr int BM = 256;           // query rows per workgroup
   static constexpr int BN = 64;            // keys per K/V tile
-  static constexpr int NT = 256;           // threads per workgroup
+  static constexpr int NT = 512;           // threads per workgroup (8 waves x 32 rows)
   static constexpr int KSTEPS = D / 16;    // 16-wide d steps of Q K^T
   static constexpr int DB = D / 32;        // 32-wide d blocks of O
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -68,6 +71,18 @@ __device__ __forceinline__ int krow_perm(int r) {
   return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Scheduling hint for the current basic block: MFMAs alternate with groups of
+// up to VPM VALU instructions, LDS reads are issued ahead of them.
+template <int NMFMA, int VPM>
+__device__ __forceinline__ void sched_interleave() {
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0); // VALU
+  }
+}
+
 // Rotate the 4 adjacent bf16 pairs of one 16-byte chunk by (cos, sin).
 __device__ __forceinline__ u32x4 rope_chunk(u32x4 x, f32x4 cs01, f32x4 cs23) {
   u32x4 y;
@@ -82,7 +97,7 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 x, f32x4 cs01, f32x4 cs23) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_kernel(AttnArgs a) {
   using C = Bf16Cfg<D>;
   __shared__ __attribute__((aligned(16))) char ksm[2][C::KTILEB];
@@ -102,194 +117,223 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   const float c = a.c;
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated, held in registers.
-  bf16x8 qf[2][C::KSTEPS];
+  const int qrow = qt * C::BM + wave * 32 + l32;
+  bf16x8 qf[C::KSTEPS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = qt * C::BM + wave * 64 + qb * 32 + l32;
-    const bool ok = row < N;
-#pragma unroll
-    for (int t = 0; t < C::KSTEPS; ++t) {
-      const int d0 = 16 * t + 8 * g;
-      u32x4 x = {0, 0, 0, 0};
-      f32x4 cs01 = {1.f, 0.f, 1.f, 0.f}, cs23 = {1.f, 0.f, 1.f, 0.f};
-      if (ok) {
-        x = global_load_b128(qbase + (size_t)row * tok_stride + d0);
-        const f32x4* rp = (const f32x4*)(a.rope + (size_t)row * (D / 2) + d0 / 2);
-        cs01 = rp[0];
-        cs23 = rp[1];
-      }
-      qf[qb][t] = __builtin_bit_cast(bf16x8, rope_chunk(x, cs01, cs23));
+  for (int t = 0; t < C::KSTEPS; ++t) {
+    const int d0 = 16 * t + 8 * g;
+    u32x4 x = {0, 0, 0, 0};
+    f32x4 cs01 = {1.f, 0.f, 1.f, 0.f}, cs23 = {1.f, 0.f, 1.f, 0.f};
+    if (qrow < N) {
+      x = global_load_b128(qbase + (size_t)qrow * tok_stride + d0);
+      const f32x4* rp = (const f32x4*)(a.rope + (size_t)qrow * (D / 2) + d0 / 2);
+      cs01 = rp[0];
+      cs23 = rp[1];
     }
+    qf[t] = __builtin_bit_cast(bf16x8, rope_chunk(x, cs01, cs23));
   }
 
-  // ---- staging of one K/V tile: global -> registers (K rotated) -> LDS.
+  // ---- staging of K/V tiles: global -> registers -> (K rotated) -> LDS.
+  // Each thread owns NPASS (row, 16-byte chunk) slots of a tile, split into two
+  // halves with separate lifetimes so that the loads of tile j+2 can be issued
+  // as soon as the matching half of tile j+1 has been written to LDS.
   const int st_chunk = tid % C::CPR;
   const int st_row0 = tid / C::CPR;
+  constexpr int HALF = C::NPASS / 2;
   u32x4 kraw[C::NPASS], vraw[C::NPASS];
   f32x4 kcs[C::NPASS][2];
-  auto stage_load = [&](int kt0) {
-#pragma unroll
-    for (int p = 0; p < C::NPASS; ++p) {
-      const int key = kt0 + st_row0 + p * C::RPP;
-      kraw[p] = (u32x4){0, 0, 0, 0};
-      vraw[p] = (u32x4){0, 0, 0, 0};
-      kcs[p][0] = (f32x4){1.f, 0.f, 1.f, 0.f};
-      kcs[p][1] = (f32x4){1.f, 0.f, 1.f, 0.f};
-      if (key < N) {
-        kraw[p] = global_load_b128(kbase + (size_t)key * tok_stride + st_chunk * 8);
-        vraw[p] = global_load_b128(vbase + (size_t)key * tok_stride + st_chunk * 8);
-        const f32x4* rp = (const f32x4*)(a.rope + (size_t)key * (D / 2) + st_chunk * 4);
-        kcs[p][0] = rp[0];
-        kcs[p][1] = rp[1];
-      }
-    }
+  // Rows past the end are clamped to row N-1: their keys are masked to -inf
+  // before the softmax, so any finite K/V content gives p = 0.  Tiles past the
+  // last one are staged the same way into a buffer that is never read.
+  auto stage_load = [&](int kt0, int p) {
+    const int key = min(kt0 + st_row0 + p * C::RPP, N - 1);
+    kraw[p] = global_load_b128(kbase + (size_t)key * tok_stride + st_chunk * 8);
+    vraw[p] = global_load_b128(vbase + (size_t)key * tok_stride + st_chunk * 8);
+    const f32x4* rp = (const f32x4*)(a.rope + (size_t)key * (D / 2) + st_chunk * 4);
+    kcs[p][0] = rp[0];
+    kcs[p][1] = rp[1];
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](int buf, int p) {
     FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
     FLUX_LDS char* vl = (FLUX_LDS char*)vsm[buf];
+    const int r = st_row0 + p * C::RPP;
+    lds_write_b128(kl + k_off<D>(r, st_chunk), rope_chunk(kraw[p], kcs[p][0], kcs[p][1]));
+    lds_write_b128(vl + v_off<D>(r, st_chunk), vraw[p]);
+  };
+
+  f32x16 o[C::DB];
 #pragma unroll
-    for (int p = 0; p < C::NPASS; ++p) {
-      const int r = st_row0 + p * C::RPP;
-      lds_write_b128(kl + k_off<D>(r, st_chunk), rope_chunk(kraw[p], kcs[p][0], kcs[p][1]));
-      lds_write_b128(vl + v_off<D>(r, st_chunk), vraw[p]);
+  for (int db = 0; db < C::DB; ++db) o[db] = (f32x16){};
+  float m_ref = -INFINITY;
+  float lsum = 0.f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int grp = lane >> 4, li = lane & 15;
+
+  // S^T block kb (32 keys x the wave's 32 queries) of a K tile in LDS.  All
+  // K fragments of the block are read before the MFMA chain starts.
+  auto qk = [&](const FLUX_LDS char* kl, int kb) -> f32x16 {
+    const int krow = 32 * kb + krow_perm(l32);
+    bf16x8 kf[C::KSTEPS];
+#pragma unroll
+    for (int t = 0; t < C::KSTEPS; ++t)
+      kf[t] = __builtin_bit_cast(bf16x8, lds_read_b128(kl + k_off<D>(krow, 2 * t + g)));
+    f32x16 s = {};
+#pragma unroll
+    for (int t = 0; t < C::KSTEPS; ++t) s = mfma_bf16(kf[t], qf[t], s);
+    return s;
+  };
+  // Keys past N (last tile only) get score -inf.
+  auto mask = [&](int kt0, int kb, f32x16& s) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kt0 + 32 * kb + 16 * (e >> 3) + 8 * g + (e & 7);
+      if (key >= N) s[e] = -INFINITY;
+    }
+  };
+  // Block max and lazy update of the running max (in the exp2 domain).  Returns
+  // whether any lane of the wave moved its reference; *alpha is the factor by
+  // which earlier partial results must be scaled (1 where nothing moved).
+  auto update_max = [&](const f32x16& s, float* alpha) -> bool {
+    float mt = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
+    mt = fmaxf(mt, swap_halves(mt));
+    const float ms = mt * c;
+    const bool need = ms > m_ref + 8.0f;
+    *alpha = 1.0f;
+    if (__ballot(need) == 0) return false;
+    *alpha = need ? __builtin_amdgcn_exp2f(m_ref - ms) : 1.0f;
+    m_ref = need ? ms : m_ref;
+    return true;
+  };
+  auto rescale_o = [&](float alpha) {
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+  };
+  // P^T fragment of one 16-key slice (hh) of block s; row sums over the
+  // bf16-rounded values.  The dot operand is built as a bf16x2 directly: a
+  // bit-cast vector element here made the compiler feed one register to every
+  // dot instruction.
+  auto make_p = [&](const f32x16& s, int hh) -> u32x4 {
+    u32x4 pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hh + 2 * i], c, -m_ref));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hh + 2 * i + 1], c, -m_ref));
+      bf16x2 pp;
+      pp[0] = (__bf16)p0;
+      pp[1] = (__bf16)p1;
+      pf[i] = __builtin_bit_cast(uint32_t, pp);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+    }
+    return pf;
+  };
+  // Multiply a packed bf16 P^T fragment by alpha (rare: the running max moved
+  // after it was formed).
+  auto scale_p = [&](u32x4& pf, float alpha) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf[i] = pack_bf16(bf16lo(pf[i]) * alpha, bf16hi(pf[i]) * alpha);
+  };
+  // O^T += V^T P^T for the 16-key slice (kb, hh).
+  auto pv = [&](const FLUX_LDS char* vl, int kb, int hh, const u32x4& pf) {
+    const int krow0 = 32 * kb + 16 * hh + 8 * (grp >> 1) + (li >> 2);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int d = 32 * db + 16 * (grp & 1) + 4 * (li & 3);
+      const int cb = (d & 7) * 2;
+      const u32x2 lo = lds_read_tr16(vl + v_off<D>(krow0, d >> 3) + cb);
+      const u32x2 hi = lds_read_tr16(vl + v_off<D>(krow0 + 4, d >> 3) + cb);
+      const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
+      o[db] = mfma_bf16(__builtin_bit_cast(bf16x8, vv), __builtin_bit_cast(bf16x8, pf), o[db]);
     }
   };
 
-  f32x16 o[2][C::DB];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) o[qb][db] = (f32x16){};
-  float m_ref[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
   const int n_tiles = (N + C::BN - 1) / C::BN;
-  stage_load(0);
-  stage_store(0);
+#pragma unroll
+  for (int p = 0; p < C::NPASS; ++p) stage_load(0, p);
+#pragma unroll
+  for (int p = 0; p < C::NPASS; ++p) stage_store(0, p);
+  if (n_tiles > 1) {
+#pragma unroll
+    for (int p = 0; p < C::NPASS; ++p) stage_load(C::BN, p);
+  }
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  // Per tile j (buffer j&1 holds tile j, buffer (j+1)&1 receives tile j+1):
+  //   1. S0 = QK(block 0)              || RoPE + LDS store of half of tile j+1
+  //   2. S1 = QK(block 1)              || P(block 0); loads of that half of tile j+2
+  //   3. O += PV(block 0, keys 0-15)   || P(block 1, keys 0-15)
+  //   4. O += PV(block 0, keys 16-31)  || P(block 1, keys 16-31)
+  //   5. O += PV(block 1)              || RoPE + store of the other half of tile j+1;
+  //                                      its loads for tile j+2
+  // The running max is checked per 32-key block; when it moves (rare after
+  // the first tile) the already packed P of block 0 is rescaled as well.
+  // One tile step; LAST selects the masked variant for a ragged final tile.
+  auto tile_step = [&](int j, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
     const int buf = j & 1;
-    if (j + 1 < n_tiles) stage_load((j + 1) * C::BN);
     const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[buf];
     const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[buf];
-
-    // ---- S^T = K Q^T for 2 key blocks x 2 query blocks.
-    f32x16 s[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb][0] = (f32x16){};
-      s[kb][1] = (f32x16){};
-      const int krow = 32 * kb + krow_perm(l32);
-#pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, lds_read_b128(kl + k_off<D>(krow, 2 * t + g)));
-        s[kb][0] = mfma_bf16(kf, qf[0][t], s[kb][0]);
-        s[kb][1] = mfma_bf16(kf, qf[1][t], s[kb][1]);
-      }
-    }
-
-    // ---- mask keys past the end (last tile only).
     const int kt0 = j * C::BN;
-    if (kt0 + C::BN > N) {
+    float alpha;
+
+    // 1. S0 = QK(block 0) || RoPE + store of the first half of tile j+1.
+    f32x16 s0 = qk(kl, 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int p = 0; p < HALF; ++p) stage_store(buf ^ 1, p);
+    sched_interleave<C::KSTEPS, 4>();
+    if (LAST) mask(kt0, 0, s0);
+    if (update_max(s0, &alpha)) rescale_o(alpha);
+
+    // 2. S1 = QK(block 1) || P of block 0; loads of the first half of tile j+2.
+    f32x16 s1 = qk(kl, 1);
+    u32x4 p00 = make_p(s0, 0);
+    u32x4 p01 = make_p(s0, 1);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kt0 + 32 * kb + 16 * (e >> 3) + 8 * g + (e & 7);
-          if (key >= N) {
-            s[kb][0][e] = -INFINITY;
-            s[kb][1][e] = -INFINITY;
-          }
-        }
+    for (int p = 0; p < HALF; ++p) stage_load((j + 2) * C::BN, p);
+    sched_interleave<C::KSTEPS, 6>();
+    if (LAST) mask(kt0, 1, s1);
+    if (update_max(s1, &alpha)) {
+      rescale_o(alpha);
+      scale_p(p00, alpha);
+      scale_p(p01, alpha);
     }
 
-    // ---- online softmax: tile row max, lazy rescale of the running state.
-    float mref[2];
+    // 3.-5. O += PV(block 0) || P of block 1; O += PV(block 1) || RoPE + store
+    // of the second half of tile j+1 and its loads for tile j+2.
+    pv(vl, 0, 0, p00);
+    u32x4 p10 = make_p(s1, 0);
+    pv(vl, 0, 1, p01);
+    u32x4 p11 = make_p(s1, 1);
+    pv(vl, 1, 0, p10);
+    pv(vl, 1, 1, p11);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mt = s[0][qb][0];
+    for (int p = HALF; p < C::NPASS; ++p) stage_store(buf ^ 1, p);
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[0][qb][e]);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[1][qb][e]);
-      mt = fmaxf(mt, swap_halves(mt));
-      const float ms = mt * c;
-      const bool need = ms > m_ref[qb] + 8.0f;
-      if (__ballot(need) != 0) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[qb] - ms) : 1.0f;
-        m_ref[qb] = need ? ms : m_ref[qb];
-        lsum[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) o[qb][db] *= alpha;
-      }
-      mref[qb] = m_ref[qb];
-    }
-
-    // ---- P = exp2(S c - m) as bf16 P^T fragments, then O^T += V^T P^T, one
-    // 16-key slice at a time.
-    const int grp = lane >> 4, li = lane & 15;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 pf[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          u32x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * hh + 2 * i], c, -mref[qb]));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * hh + 2 * i + 1], c, -mref[qb]));
-            // Row sums over the bf16-rounded P (the values the PV product uses).
-            // The dot operand is built as a bf16x2 directly: passing a bit-cast
-            // element of w here made the compiler feed the same register to
-            // every dot instruction.
-            bf16x2 pp;
-            pp[0] = (__bf16)p0;
-            pp[1] = (__bf16)p1;
-            w[i] = __builtin_bit_cast(uint32_t, pp);
-            lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum[qb], false);
-          }
-          pf[qb] = __builtin_bit_cast(bf16x8, w);
-        }
-        const int krow0 = 32 * kb + 16 * hh + 8 * (grp >> 1) + (li >> 2);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const int d = 32 * db + 16 * (grp & 1) + 4 * (li & 3);
-          const int cb = (d & 7) * 2;
-          const u32x2 lo = lds_read_tr16(vl + v_off<D>(krow0, d >> 3) + cb);
-          const u32x2 hi = lds_read_tr16(vl + v_off<D>(krow0 + 4, d >> 3) + cb);
-          const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
-          o[0][db] = mfma_bf16(vf, pf[0], o[0][db]);
-          o[1][db] = mfma_bf16(vf, pf[1], o[1][db]);
-        }
-      }
-
-    if (j + 1 < n_tiles) stage_store(buf ^ 1);
+    for (int p = HALF; p < C::NPASS; ++p) stage_load((j + 2) * C::BN, p);
+    sched_interleave<4 * C::DB, 5>();
     __syncthreads();
-  }
+  };
+
+  const int n_full = N / C::BN;
+  for (int j = 0; j < n_full; ++j) tile_step(j, std::false_type{});
+  if (n_full < n_tiles) tile_step(n_full, std::true_type{});
 
   // ---- epilogue: O = O^T / l, bf16, stored row-major.
+  const float inv = 1.0f / (lsum + swap_halves(lsum));
+  if (qrow < N) {
+    uint16_t* orow = a.o + (size_t)b * N * tok_stride + (size_t)qrow * tok_stride + (size_t)h * D;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = qt * C::BM + wave * 64 + qb * 32 + l32;
-    const float inv = 1.0f / (lsum[qb] + swap_halves(lsum[qb]));
-    if (row < N) {
-      uint16_t* orow = a.o + (size_t)b * N * tok_stride + (size_t)row * tok_stride + (size_t)h * D;
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int aa = 0; aa < 4; ++aa) {
-          const int d = 32 * db + 8 * aa + 4 * g;
-          u32x2 w;
-          w[0] = pack_bf16(o[qb][db][4 * aa + 0] * inv, o[qb][db][4 * aa + 1] * inv);
-          w[1] = pack_bf16(o[qb][db][4 * aa + 2] * inv, o[qb][db][4 * aa + 3] * inv);
-          *(u32x2*)(orow + d) = w;
-        }
-    }
+      for (int aa = 0; aa < 4; ++aa) {
+        const int d = 32 * db + 8 * aa + 4 * g;
+        u32x2 w;
+        w[0] = pack_bf16(o[db][4 * aa + 0] * inv, o[db][4 * aa + 1] * inv);
+        w[1] = pack_bf16(o[db][4 * aa + 2] * inv, o[db][4 * aa + 3] * inv);
+        *(u32x2*)(orow + d) = w;
+      }
   }
 }
 
@@ -299,9 +343,9 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t stream)
   AttnArgs args = a;
   args.q_tiles = q_tiles;
   if (head_dim == 128)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(grid), dim3(Bf16Cfg<128>::NT), 0, stream, args);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(grid), dim3(Bf16Cfg<64>::NT), 0, stream, args);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -60,7 +60,21 @@ struct flux_attn_plan {
   int device = -1;
   float2* rope_table = nullptr;  // [max_tokens][head_dim/2]
   double* freq = nullptr;        // [head_dim/2]
+  std::vector<hipEvent_t> ev_start, ev_stop;  // kernel timing pairs
+  int timing_used = 0;
 };
+
+namespace {
+
+void release_timing(flux_attn_plan* p) {
+  for (auto e : p->ev_start) (void)hipEventDestroy(e);
+  for (auto e : p->ev_stop) (void)hipEventDestroy(e);
+  p->ev_start.clear();
+  p->ev_stop.clear();
+  p->timing_used = 0;
+}
+
+}  // namespace
 
 namespace {
 
@@ -253,8 +267,61 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
   a.heads = c.num_heads;
   a.batch = c.batch;
   a.c = scale * log2e;
+  const bool timed = plan->timing_used < (int)plan->ev_start.size();
+  if (timed) {
+    e = hipEventRecord(plan->ev_start[plan->timing_used], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
   e = flux::launch_attn_bf16(a, c.head_dim, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (timed) {
+    e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    ++plan->timing_used;
+  }
+  return ok();
+}
+
+int flux_attn_timing_enable(flux_attn_plan* plan, int32_t capacity) {
+  if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
+  if (capacity < 0 || capacity > 4096)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "timing capacity %d outside [0, 4096]", capacity);
+  release_timing(plan);
+  for (int i = 0; i < capacity; ++i) {
+    hipEvent_t a, b;
+    hipError_t e = hipEventCreate(&a);
+    if (e != hipSuccess) {
+      release_timing(plan);
+      return hip_fail(e, "hipEventCreate");
+    }
+    e = hipEventCreate(&b);
+    if (e != hipSuccess) {
+      (void)hipEventDestroy(a);
+      release_timing(plan);
+      return hip_fail(e, "hipEventCreate");
+    }
+    plan->ev_start.push_back(a);
+    plan->ev_stop.push_back(b);
+  }
+  return ok();
+}
+
+int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, int32_t max_count, int32_t* count) {
+  if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
+  if (!count || (max_count > 0 && !attn_ms)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "output pointer is NULL");
+  *count = 0;
+  const int n = plan->timing_used;
+  if (n > 0) {
+    hipError_t e = hipEventSynchronize(plan->ev_stop[n - 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    const int m = n < max_count ? n : max_count;
+    for (int i = 0; i < m; ++i) {
+      e = hipEventElapsedTime(&attn_ms[i], plan->ev_start[i], plan->ev_stop[i]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    }
+    *count = m;
+  }
+  plan->timing_used = 0;
   return ok();
 }
 
@@ -264,6 +331,7 @@ int flux_attn_destroy(flux_attn_plan* plan) {
     std::lock_guard<std::mutex> lk(g_plans_mu);
     if (!g_plans.erase(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is not live (destroyed or foreign)");
   }
+  release_timing(plan);
   hipError_t e1 = hipFree(plan->rope_table);
   hipError_t e2 = hipFree(plan->freq);
   delete plan;

@@ -71,6 +71,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flux_attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "flux_attn_last_error": ([], ctypes.c_char_p),
         "flux_attn_abi_version": ([], ctypes.c_int),
+        "flux_attn_timing_enable": ([_vp, _i32], ctypes.c_int),
+        "flux_attn_timing_read": ([_vp, ctypes.POINTER(ctypes.c_float), _i32, _i32p], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -182,6 +184,17 @@ class Plan:
                                           segs, len(segment_tokens), pos_ids.data_ptr(), out.data_ptr(),
                                           _MODES[mode], stream.cuda_stream), "forward")
         return out
+
+    def timing_enable(self, capacity: int) -> None:
+        """Record the attention kernel's duration for the next ``capacity`` forwards."""
+        check(self._lib.flux_attn_timing_enable(self._handle, int(capacity)), "timing_enable")
+
+    def timing_read(self, max_count: int = 4096) -> list:
+        """Durations (ms) of the attention kernels recorded since timing_enable/last read."""
+        buf = (ctypes.c_float * max_count)()
+        n = ctypes.c_int32(0)
+        check(self._lib.flux_attn_timing_read(self._handle, buf, max_count, ctypes.byref(n)), "timing_read")
+        return [buf[i] for i in range(n.value)]
 
     def close(self) -> None:
         if getattr(self, "_handle", None) is not None:

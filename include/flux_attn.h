@@ -110,6 +110,17 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
                       int32_t num_segments, const int32_t* pos_ids, void* out,
                       int32_t mode, void* hip_stream);
 
+/* Kernel timing.  flux_attn_timing_enable(plan, capacity) with capacity > 0
+ * creates capacity pairs of HIP events (capacity <= 4096); every following
+ * forward() records one pair around its attention kernel (none once all pairs
+ * are used), on the stream that kernel runs on.  capacity = 0 releases them.
+ * flux_attn_timing_read() waits for the last recorded pair, writes the
+ * durations in milliseconds of up to max_count recorded launches to
+ * attn_ms[0..*count-1] (host array) and starts over.  The caller must not
+ * read while another thread runs forward() on the plan. */
+int flux_attn_timing_enable(flux_attn_plan* plan, int32_t capacity);
+int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, int32_t max_count, int32_t* count);
+
 /* Copies the plan's configuration into *cfg. */
 int flux_attn_get_config(const flux_attn_plan* plan, flux_attn_config* cfg);
 
