@@ -96,6 +96,20 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 x, f32x4 cs01, f32x4 cs23) {
   return y;
 }
 
+// Same rotation, result multiplied by k before rounding (Q carries the
+// softmax scale times log2(e)).
+__device__ __forceinline__ u32x4 rope_chunk_scaled(u32x4 x, f32x4 cs01, f32x4 cs23, float k) {
+  u32x4 y;
+  float c[4] = {cs01[0], cs01[2], cs23[0], cs23[2]};
+  float s[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x0 = bf16lo(x[i]), x1 = bf16hi(x[i]);
+    y[i] = pack_bf16((x0 * c[i] - x1 * s[i]) * k, (x0 * s[i] + x1 * c[i]) * k);
+  }
+  return y;
+}
+
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_kernel(AttnArgs a) {
@@ -104,7 +118,17 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char vsm[2][C::VTILEB];
 
   const int N = a.n_tokens, H = a.heads;
-  const int tile = xcd_tile_order(blockIdx.x, gridDim.x);
+  const int n_tiles = (N + C::BN - 1) / C::BN;
+  int tile, kv0 = 0, kv1 = n_tiles, slot = -1;
+  if ((int)blockIdx.x < a.whole) {
+    tile = xcd_tile_order(blockIdx.x, a.whole);
+  } else {
+    slot = blockIdx.x - a.whole;
+    tile = a.whole + slot / a.split;
+    const int piece = slot % a.split;
+    kv0 = piece * n_tiles / a.split;
+    kv1 = (piece + 1) * n_tiles / a.split;
+  }
   const int qt = tile % a.q_tiles;
   const int bh = tile / a.q_tiles;
   const int h = bh % H, b = bh / H;
@@ -130,8 +154,15 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
       cs01 = rp[0];
       cs23 = rp[1];
     }
-    qf[t] = __builtin_bit_cast(bf16x8, rope_chunk(x, cs01, cs23));
+    qf[t] = __builtin_bit_cast(bf16x8, rope_chunk_scaled(x, cs01, cs23, c));
   }
+  // Running max folded into the score MFMA: an extra k-step multiplies a
+  // column of ones in K by -m in Q, so the accumulator holds c*s - m and
+  // p = exp2(acc).  m is kept bf16-representable, so this is exact.  Lanes of
+  // the first half-wave carry k index 0 of the step, the others zeros.
+  const bf16x8 zero8 = {};
+  bf16x8 kone = zero8, qm = zero8;
+  if (g == 0) kone[0] = (__bf16)1.0f;
 
   // ---- staging of K/V tiles: global -> registers -> (K rotated) -> LDS.
   // Each thread owns NPASS (row, 16-byte chunk) slots of a tile, split into two
@@ -142,16 +173,29 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int HALF = C::NPASS / 2;
   u32x4 kraw[C::NPASS], vraw[C::NPASS];
   f32x4 kcs[C::NPASS][2];
-  // Rows past the end are clamped to row N-1: their keys are masked to -inf
-  // before the softmax, so any finite K/V content gives p = 0.  Tiles past the
-  // last one are staged the same way into a buffer that is never read.
+  // Buffer loads relative to the tile's first row: rows at or past N read as
+  // zero (their keys are masked to -inf before the softmax), and tiles past
+  // the last one are staged as zeros into a buffer that is never read.  The
+  // per-thread offsets are loop invariant; the tile offset goes into the
+  // (scalar) resource base.
+  uint32_t kv_off[C::NPASS], rp_off[C::NPASS];
+#pragma unroll
+  for (int p = 0; p < C::NPASS; ++p) {
+    const int r = st_row0 + p * C::RPP;
+    kv_off[p] = (uint32_t)(r * tok_stride * 2 + st_chunk * 16);
+    rp_off[p] = (uint32_t)(r * (D / 2) * 8 + st_chunk * 32);
+  }
   auto stage_load = [&](int kt0, int p) {
-    const int key = min(kt0 + st_row0 + p * C::RPP, N - 1);
-    kraw[p] = global_load_b128(kbase + (size_t)key * tok_stride + st_chunk * 8);
-    vraw[p] = global_load_b128(vbase + (size_t)key * tok_stride + st_chunk * 8);
-    const f32x4* rp = (const f32x4*)(a.rope + (size_t)key * (D / 2) + st_chunk * 4);
-    kcs[p][0] = rp[0];
-    kcs[p][1] = rp[1];
+    const int rows = N - kt0;
+    const uint32_t kv_bytes = rows > 0 ? (uint32_t)((rows - 1) * tok_stride * 2 + 2 * D) : 0u;
+    const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 8) : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, kv_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)kt0 * tok_stride, kv_bytes);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rope + (size_t)kt0 * (D / 2), rp_bytes);
+    kraw[p] = buffer_load_b128(rk, kv_off[p]);
+    vraw[p] = buffer_load_b128(rv, kv_off[p]);
+    kcs[p][0] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off[p]));
+    kcs[p][1] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off[p] + 16));
   };
   auto stage_store = [&](int buf, int p) {
     FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
@@ -164,7 +208,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   f32x16 o[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) o[db] = (f32x16){};
-  float m_ref = -INFINITY;
+  float m_ref = 0.f;   // running max of c*score, exp2 domain, bf16-representable
   float lsum = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int grp = lane >> 4, li = lane & 15;
@@ -177,7 +221,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < C::KSTEPS; ++t)
       kf[t] = __builtin_bit_cast(bf16x8, lds_read_b128(kl + k_off<D>(krow, 2 * t + g)));
-    f32x16 s = {};
+    f32x16 s = mfma_bf16(kone, qm, (f32x16){});
 #pragma unroll
     for (int t = 0; t < C::KSTEPS; ++t) s = mfma_bf16(kf[t], qf[t], s);
     return s;
@@ -193,17 +237,26 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   // Block max and lazy update of the running max (in the exp2 domain).  Returns
   // whether any lane of the wave moved its reference; *alpha is the factor by
   // which earlier partial results must be scaled (1 where nothing moved).
-  auto update_max = [&](const f32x16& s, float* alpha) -> bool {
+  // s holds c*score - m_ref.  The first block of a range always sets m_ref to
+  // its (bf16-rounded) max; later blocks move it only when a row exceeds it
+  // by more than 8.  When it moves, s is re-based on the new m_ref and *alpha
+  // is the factor for everything accumulated so far (0 on the first block,
+  // where nothing has been).
+  auto update_max = [&](f32x16& s, bool first, float* alpha) -> bool {
     float mt = s[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
     mt = fmaxf(mt, swap_halves(mt));
-    const float ms = mt * c;
-    const bool need = ms > m_ref + 8.0f;
+    const bool need = first || mt > 8.0f;
     *alpha = 1.0f;
     if (__ballot(need) == 0) return false;
-    *alpha = need ? __builtin_amdgcn_exp2f(m_ref - ms) : 1.0f;
-    m_ref = need ? ms : m_ref;
+    const float m_new = need ? bf16_round(m_ref + mt) : m_ref;
+    const float shift = m_ref - m_new;
+    *alpha = first ? 0.0f : __builtin_amdgcn_exp2f(shift);
+    m_ref = m_new;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] += shift;
+    if (g == 0) qm[0] = (__bf16)(-m_new);
     return true;
   };
   auto rescale_o = [&](float alpha) {
@@ -219,8 +272,8 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     u32x4 pf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hh + 2 * i], c, -m_ref));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hh + 2 * i + 1], c, -m_ref));
+      const float p0 = __builtin_amdgcn_exp2f(s[8 * hh + 2 * i]);
+      const float p1 = __builtin_amdgcn_exp2f(s[8 * hh + 2 * i + 1]);
       bf16x2 pp;
       pp[0] = (__bf16)p0;
       pp[1] = (__bf16)p1;
@@ -249,15 +302,12 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     }
   };
 
-  const int n_tiles = (N + C::BN - 1) / C::BN;
 #pragma unroll
-  for (int p = 0; p < C::NPASS; ++p) stage_load(0, p);
+  for (int p = 0; p < C::NPASS; ++p) stage_load(kv0 * C::BN, p);
 #pragma unroll
   for (int p = 0; p < C::NPASS; ++p) stage_store(0, p);
-  if (n_tiles > 1) {
 #pragma unroll
-    for (int p = 0; p < C::NPASS; ++p) stage_load(C::BN, p);
-  }
+  for (int p = 0; p < C::NPASS; ++p) stage_load((kv0 + 1) * C::BN, p);
   __syncthreads();
 
   // Per tile j (buffer j&1 holds tile j, buffer (j+1)&1 receives tile j+1):
@@ -272,7 +322,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   // One tile step; LAST selects the masked variant for a ragged final tile.
   auto tile_step = [&](int j, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
-    const int buf = j & 1;
+    const int buf = (j - kv0) & 1;
     const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[buf];
     const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[buf];
     const int kt0 = j * C::BN;
@@ -284,7 +334,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int p = 0; p < HALF; ++p) stage_store(buf ^ 1, p);
     sched_interleave<C::KSTEPS, 4>();
     if (LAST) mask(kt0, 0, s0);
-    if (update_max(s0, &alpha)) rescale_o(alpha);
+    if (update_max(s0, j == kv0, &alpha)) rescale_o(alpha);
 
     // 2. S1 = QK(block 1) || P of block 0; loads of the first half of tile j+2.
     f32x16 s1 = qk(kl, 1);
@@ -294,7 +344,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int p = 0; p < HALF; ++p) stage_load((j + 2) * C::BN, p);
     sched_interleave<C::KSTEPS, 6>();
     if (LAST) mask(kt0, 1, s1);
-    if (update_max(s1, &alpha)) {
+    if (update_max(s1, false, &alpha)) {
       rescale_o(alpha);
       scale_p(p00, alpha);
       scale_p(p01, alpha);
@@ -316,12 +366,27 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     __syncthreads();
   };
 
-  const int n_full = N / C::BN;
-  for (int j = 0; j < n_full; ++j) tile_step(j, std::false_type{});
-  if (n_full < n_tiles) tile_step(n_full, std::true_type{});
+  const int full_end = min(kv1, N / C::BN);  // tiles before this one are full
+  for (int j = kv0; j < full_end; ++j) tile_step(j, std::false_type{});
+  if (full_end < kv1) tile_step(full_end, std::true_type{});
 
+  // ---- epilogue.  A K/V range of a split tile stores its fp32 partial state.
+  const float ltot = lsum + swap_halves(lsum);
+  if (slot >= 0) {
+    const int r = wave * 32 + l32;
+    float* po = a.part_o + ((size_t)slot * C::BM + r) * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        const f32x4 w = {o[db][4 * aa], o[db][4 * aa + 1], o[db][4 * aa + 2], o[db][4 * aa + 3]};
+        *(f32x4*)(po + 32 * db + 8 * aa + 4 * g) = w;
+      }
+    if (g == 0) a.part_ml[(size_t)slot * C::BM + r] = make_float2(m_ref, ltot);
+    return;
+  }
   // ---- epilogue: O = O^T / l, bf16, stored row-major.
-  const float inv = 1.0f / (lsum + swap_halves(lsum));
+  const float inv = 1.0f / ltot;
   if (qrow < N) {
     uint16_t* orow = a.o + (size_t)b * N * tok_stride + (size_t)qrow * tok_stride + (size_t)h * D;
 #pragma unroll
@@ -337,15 +402,67 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   }
 }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t stream) {
-  const int q_tiles = (a.n_tokens + 255) / 256;
-  const int grid = q_tiles * a.heads * a.batch;
+// One thread per (split tile, row, 8 output dims): combines the `split`
+// partial states of its row exactly and writes bf16.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  const int per_tile = 256 * (D / 8);
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int st = idx / per_tile;
+  const int rem = idx - st * per_tile;
+  const int r = rem / (D / 8), d0 = (rem % (D / 8)) * 8;
+  const int tile = a.whole + st;
+  const int qt = tile % a.q_tiles, bh = tile / a.q_tiles;
+  const int h = bh % a.heads, b = bh / a.heads;
+  const int row = qt * 256 + r;
+  if (row >= a.n_tokens) return;
+  const int slot0 = st * a.split;
+  float m = -INFINITY;
+  for (int i = 0; i < a.split; ++i) m = fmaxf(m, a.part_ml[(size_t)(slot0 + i) * 256 + r].x);
+  float l = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = 0; i < a.split; ++i) {
+    const float2 ml = a.part_ml[(size_t)(slot0 + i) * 256 + r];
+    const float w = __builtin_amdgcn_exp2f(ml.x - m);
+    l += w * ml.y;
+    const float* po = a.part_o + ((size_t)(slot0 + i) * 256 + r) * D + d0;
+    const f32x4 x0 = *(const f32x4*)po, x1 = *(const f32x4*)(po + 4);
+    acc[0] += w * x0[0]; acc[1] += w * x0[1]; acc[2] += w * x0[2]; acc[3] += w * x0[3];
+    acc[4] += w * x1[0]; acc[5] += w * x1[1]; acc[6] += w * x1[2]; acc[7] += w * x1[3];
+  }
+  const float inv = 1.0f / l;
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  const size_t tok_stride = (size_t)a.heads * D;
+  *(u32x4*)(a.o + (size_t)b * a.n_tokens * tok_stride + (size_t)row * tok_stride + (size_t)h * D + d0) = out;
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream) {
   AttnArgs args = a;
-  args.q_tiles = q_tiles;
+  args.q_tiles = (a.n_tokens + 255) / 256;
+  args.whole = sch.whole_tiles;
+  args.split = sch.split;
   if (head_dim == 128)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(grid), dim3(Bf16Cfg<128>::NT), 0, stream, args);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(sch.grid), dim3(Bf16Cfg<128>::NT), 0, stream, args);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(grid), dim3(Bf16Cfg<64>::NT), 0, stream, args);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(sch.grid), dim3(Bf16Cfg<64>::NT), 0, stream, args);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream) {
+  if (sch.split_tiles == 0) return hipSuccess;
+  AttnArgs args = a;
+  args.q_tiles = (a.n_tokens + 255) / 256;
+  args.whole = sch.whole_tiles;
+  args.split = sch.split;
+  const int threads = sch.split_tiles * 256 * (head_dim / 8);
+  const int blocks = (threads + 255) / 256;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(256), 0, stream, args);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(256), 0, stream, args);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -63,6 +63,24 @@ __device__ __forceinline__ u32x4 global_load_b128(const void* p) {
   return *(const u32x4*)p;
 }
 
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return 0 (hardware range check), which zero-fills rows past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buffer_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voffset, 0, 0));
+}
+
+__device__ __forceinline__ float bf16_round(float x) {
+  return (float)(__bf16)x;
+}
+
 // Value of lane l ^ 32 (the other half of the wave).
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32);

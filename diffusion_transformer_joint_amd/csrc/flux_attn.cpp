@@ -60,6 +60,10 @@ struct flux_attn_plan {
   int device = -1;
   float2* rope_table = nullptr;  // [max_tokens][head_dim/2]
   double* freq = nullptr;        // [head_dim/2]
+  float* part_o = nullptr;       // split-K/V partials: [max_pieces][256][head_dim]
+  float2* part_ml = nullptr;     // [max_pieces][256]
+  int num_cus = 0;
+  int max_pieces = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;  // kernel timing pairs
   int timing_used = 0;
 };
@@ -211,12 +215,32 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     for (int j = 0; j < d / 2; ++j) freq[j0 + j] = std::pow((double)cfg->rope_theta, -2.0 * j / d);
     j0 += d / 2;
   }
+  e = hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  // Split-K/V partials: at most 4 pieces per compute unit, and no more than
+  // the launch can produce at max_tokens.
+  {
+    const long tiles = (long)cfg->batch * cfg->num_heads * ((cfg->max_tokens + 255) / 256);
+    const long kv = (cfg->max_tokens + 63) / 64;
+    long cap = 4L * p->num_cus;
+    const long most = tiles * (kv < 16 ? kv : 16);
+    p->max_pieces = (int)(cap < most ? cap : most);
+  }
   e = hipMalloc(&p->rope_table, (size_t)cfg->max_tokens * half * sizeof(float2));
   if (e == hipSuccess) e = hipMalloc(&p->freq, half * sizeof(double));
   if (e == hipSuccess) e = hipMemcpy(p->freq, freq.data(), half * sizeof(double), hipMemcpyHostToDevice);
+  if (e == hipSuccess && p->max_pieces > 0)
+    e = hipMalloc(&p->part_o, (size_t)p->max_pieces * 256 * cfg->head_dim * sizeof(float));
+  if (e == hipSuccess && p->max_pieces > 0)
+    e = hipMalloc(&p->part_ml, (size_t)p->max_pieces * 256 * sizeof(float2));
   if (e != hipSuccess) {
     (void)hipFree(p->rope_table);
     (void)hipFree(p->freq);
+    (void)hipFree(p->part_o);
+    (void)hipFree(p->part_ml);
     delete p;
     return hip_fail(e, "plan workspace");
   }
@@ -267,18 +291,37 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
   a.heads = c.num_heads;
   a.batch = c.batch;
   a.c = scale * log2e;
+  a.part_o = plan->part_o;
+  a.part_ml = plan->part_ml;
+  const int tiles = c.batch * c.num_heads * ((n + 255) / 256);
+  const flux::Schedule sch = flux::plan_schedule(tiles, (n + 63) / 64, plan->num_cus, plan->max_pieces, c.head_dim);
   const bool timed = plan->timing_used < (int)plan->ev_start.size();
   if (timed) {
     e = hipEventRecord(plan->ev_start[plan->timing_used], stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
-  e = flux::launch_attn_bf16(a, c.head_dim, stream);
+  e = flux::launch_attn_bf16(a, c.head_dim, sch, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  e = flux::launch_attn_merge(a, c.head_dim, sch, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
   if (timed) {
     e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     ++plan->timing_used;
   }
+  return ok();
+}
+
+int flux_attn_schedule(int32_t tiles, int32_t kv_tiles, int32_t num_cus, int32_t max_pieces, int32_t head_dim,
+                       int32_t* whole_tiles, int32_t* split_tiles, int32_t* split, int32_t* grid) {
+  if (!whole_tiles || !split_tiles || !split || !grid) return fail(FLUX_ATTN_INVALID_ARGUMENT, "output is NULL");
+  if (tiles < 0 || kv_tiles < 1 || num_cus < 1 || max_pieces < 0 || (head_dim != 64 && head_dim != 128))
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "bad schedule arguments");
+  const flux::Schedule s = flux::plan_schedule(tiles, kv_tiles, num_cus, max_pieces, head_dim);
+  *whole_tiles = s.whole_tiles;
+  *split_tiles = s.split_tiles;
+  *split = s.split;
+  *grid = s.grid;
   return ok();
 }
 
@@ -332,6 +375,8 @@ int flux_attn_destroy(flux_attn_plan* plan) {
     if (!g_plans.erase(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is not live (destroyed or foreign)");
   }
   release_timing(plan);
+  (void)hipFree(plan->part_o);
+  (void)hipFree(plan->part_ml);
   hipError_t e1 = hipFree(plan->rope_table);
   hipError_t e2 = hipFree(plan->freq);
   delete plan;

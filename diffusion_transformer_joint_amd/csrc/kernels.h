@@ -16,7 +16,26 @@ struct AttnArgs {
   int batch;
   int q_tiles;            // filled by the launcher
   float c;                // softmax scale * log2(e)
+  // Work split (see Schedule): blocks [0, whole) run whole query tiles; the
+  // other blocks run one of `split` K/V ranges of the remaining tiles and write
+  // fp32 partials that attn_merge combines.
+  int whole;
+  int split;
+  float* part_o;          // [slot][256][D] un-normalized O of each partial
+  float2* part_ml;        // [slot][256] (running max in the exp2 domain, row sum)
 };
+
+// How one launch covers T query tiles of 256 rows with K/V ranges of n_kv
+// 64-key tiles on C compute units (one workgroup per CU): `whole_tiles` tiles
+// are run whole, the remaining `split_tiles` are cut into `split` K/V ranges
+// each, so that the last round of workgroups fills the machine.
+struct Schedule {
+  int whole_tiles;
+  int split_tiles;
+  int split;
+  int grid;
+};
+Schedule plan_schedule(int tiles, int kv_tiles, int num_cus, int max_pieces, int head_dim);
 
 struct Fp8Args {
   const uint8_t* q;       // [B][N][H][D] e4m3 codes
@@ -36,7 +55,9 @@ struct Fp8Args {
 hipError_t launch_rope_table(const int32_t* pos, const double* freq, float2* table, int n_tokens,
                              int head_dim, int d0, int d1, hipStream_t stream);
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream);
+// Exact merge of split partials: O = sum_i 2^(m_i - m) O_i / sum_i 2^(m_i - m) l_i.
+hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream);
 hipError_t launch_attn_fp8(const Fp8Args& a, int head_dim, hipStream_t stream);
 
 }  // namespace flux

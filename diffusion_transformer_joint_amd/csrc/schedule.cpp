@@ -1,0 +1,46 @@
+// Host policy for covering the query tiles of one launch with workgroups.
+//
+// The attention kernel runs one 256-row query tile of one (batch, head) per
+// workgroup and one workgroup per compute unit.  With T tiles and C units the
+// last round is partial unless C divides T (8,704 tokens x 24 heads: 816 tiles
+// on 256 units is 3.19 rounds).  The remedy: run the first F' full rounds as
+// whole tiles and cut each of the remaining L tiles into S key/value ranges, so
+// the last round holds L*S <= C-ish short pieces; the pieces' fp32 partial
+// softmax states are merged exactly afterwards.  (F', S) minimises
+//   F' + ceil(L*S / C) / S + (merge traffic of L*S partials, in rounds).
+#include <cmath>
+
+#include "kernels.h"
+
+namespace flux {
+
+Schedule plan_schedule(int tiles, int kv_tiles, int num_cus, int max_pieces, int head_dim) {
+  Schedule best{tiles, 0, 1, tiles};
+  if (tiles <= 0 || num_cus <= 0) return best;
+  const double C = num_cus;
+  double best_cost = std::ceil(tiles / C);
+  // Time of one round of whole tiles and HBM cost of one partial (written and
+  // read back: 256 rows x head_dim fp32 + (m, l)), for the traffic penalty.
+  const double tile_s = 2.5e-6 * head_dim / 128.0;  // one 64-key step of a 256-row tile
+  const double round_s = kv_tiles * tile_s;
+  const double piece_bytes = 2.0 * 256.0 * (head_dim * 4.0 + 8.0);
+  const double hbm = 6.0e12;
+  const int F = tiles / num_cus;
+  for (int Fp = F; Fp >= 0 && Fp >= F - 1; --Fp) {
+    const int L = tiles - Fp * num_cus;
+    if (L <= 0) continue;
+    const int smax = kv_tiles < 16 ? kv_tiles : 16;
+    for (int S = 2; S <= smax; ++S) {
+      const long pieces = (long)L * S;
+      if (pieces > max_pieces) break;
+      const double cost = Fp + std::ceil(pieces / C) / S + pieces * piece_bytes / hbm / round_s;
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = Schedule{Fp * num_cus, L, S, Fp * num_cus + (int)pieces};
+      }
+    }
+  }
+  return best;
+}
+
+}  // namespace flux

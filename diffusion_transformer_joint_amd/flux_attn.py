@@ -72,6 +72,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flux_attn_last_error": ([], ctypes.c_char_p),
         "flux_attn_abi_version": ([], ctypes.c_int),
         "flux_attn_timing_enable": ([_vp, _i32], ctypes.c_int),
+        "flux_attn_schedule": ([_i32, _i32, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p], ctypes.c_int),
         "flux_attn_timing_read": ([_vp, ctypes.POINTER(ctypes.c_float), _i32, _i32p], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -115,6 +116,15 @@ def default_config(batch: int, num_heads: int, head_dim: int, max_tokens: int, d
     cfg.max_segments = max_segments
     cfg.dtype = {"bf16": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3}[dtype]
     return cfg
+
+
+def schedule(tiles: int, kv_tiles: int, num_cus: int, max_pieces: int, head_dim: int = 128) -> dict:
+    """The library's work split for one launch (host-side policy, no GPU needed)."""
+    lib = load_library()
+    out = [ctypes.c_int32() for _ in range(4)]
+    check(lib.flux_attn_schedule(tiles, kv_tiles, num_cus, max_pieces, head_dim, *[ctypes.byref(x) for x in out]),
+          "schedule")
+    return dict(zip(("whole_tiles", "split_tiles", "split", "grid"), (x.value for x in out)))
 
 
 def _i32_array(values: Sequence[int]):

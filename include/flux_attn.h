@@ -121,6 +121,17 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
 int flux_attn_timing_enable(flux_attn_plan* plan, int32_t capacity);
 int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, int32_t max_count, int32_t* count);
 
+/* Work split chosen by forward() for a launch (host only, no device call).
+ * The kernel runs one 256-row query tile of one (batch, head) per workgroup,
+ * one workgroup per compute unit.  Of `tiles` tiles, *whole_tiles run over all
+ * kv_tiles 64-key tiles; the remaining *split_tiles are each cut into *split
+ * key/value ranges whose fp32 partial softmax states are merged exactly, so
+ * that the last round of workgroups fills num_cus units.  At most max_pieces
+ * ranges are used.  *grid = *whole_tiles + *split_tiles * *split. */
+int flux_attn_schedule(int32_t tiles, int32_t kv_tiles, int32_t num_cus, int32_t max_pieces,
+                       int32_t head_dim, int32_t* whole_tiles, int32_t* split_tiles,
+                       int32_t* split, int32_t* grid);
+
 /* Copies the plan's configuration into *cfg. */
 int flux_attn_get_config(const flux_attn_plan* plan, flux_attn_config* cfg);
 
