@@ -58,6 +58,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     if not os.path.exists(p):
         raise FluxAttnError(DEVICE_ERROR, f"{p} is missing: build it with "
                             "`python -m diffusion_transformer_joint_amd.build`")
+    # torch ships its own HIP runtime under the same soname; load it first so
+    # that the library binds to that one instead of pulling in a second copy.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(p)
     cp = ctypes.POINTER(Config)
     sig = {

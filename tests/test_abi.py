@@ -136,3 +136,43 @@ def test_plan_handles_rejected_without_dereference(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(fa.FluxAttnError):
         fa.load_library(str(tmp_path / "nope.so"))
+
+
+# ---------------------------------------------------------------------------
+# host scheduling policy (split of the last round of query tiles)
+
+@pytest.mark.parametrize("tiles,kv,cus", [(816, 136, 256), (432, 72, 256), (102, 136, 256), (2352, 392, 256),
+                                          (2, 2, 256), (256, 136, 256), (512, 64, 256), (6192, 1032, 256),
+                                          (1, 1, 256), (300, 5, 80)])
+def test_schedule_invariants(tiles, kv, cus):
+    cap = 4 * cus
+    s = fa.schedule(tiles, kv, cus, cap)
+    assert s["whole_tiles"] + s["split_tiles"] == tiles
+    assert s["grid"] == s["whole_tiles"] + s["split_tiles"] * s["split"]
+    assert 1 <= s["split"] <= max(1, min(16, kv))
+    if s["split_tiles"]:
+        assert s["split"] >= 2 and s["split_tiles"] * s["split"] <= cap
+        assert s["whole_tiles"] % cus == 0          # whole tiles fill complete rounds
+    else:
+        assert s["split"] == 1 and s["grid"] == tiles
+
+
+def test_schedule_no_split_when_rounds_are_full():
+    for tiles in (256, 512, 768):
+        s = fa.schedule(tiles, 136, 256, 1024)
+        assert s["split_tiles"] == 0 and s["grid"] == tiles
+
+
+def test_schedule_fills_last_round():
+    # 8,704 tokens x 24 heads: 816 tiles = 3.19 rounds on 256 units; the 48 left
+    # over are cut so the final round is short instead of a fourth full round
+    s = fa.schedule(816, 136, 256, 1024)
+    assert s["whole_tiles"] == 768 and s["split_tiles"] == 48 and s["split"] >= 4
+    # one GPU's share of an 8-way head split (3 heads): fewer tiles than units
+    s = fa.schedule(102, 136, 256, 1024)
+    assert s["whole_tiles"] == 0 and s["split"] >= 2 and s["grid"] >= 200
+
+
+def test_schedule_respects_piece_cap():
+    s = fa.schedule(432, 72, 256, 300)
+    assert s["split_tiles"] * s["split"] <= 300 or s["split_tiles"] == 0
