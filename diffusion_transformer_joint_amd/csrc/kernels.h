@@ -41,7 +41,7 @@ struct Fp8Args {
   const uint8_t* q;       // [B][N][H][D] e4m3 codes
   const uint8_t* k;
   const uint8_t* v;
-  const float* scales;    // [3][B][H]
+  const float* scales;    // [3][B][H]: q, k, v scales
   uint16_t* o;            // [B][N][H][D] bf16 bits
   const float2* rope;     // [N][D/2]
   int n_tokens;
@@ -49,6 +49,10 @@ struct Fp8Args {
   int batch;
   int q_tiles;
   float c;
+  int whole;
+  int split;
+  float* part_o;
+  float2* part_ml;
 };
 
 // (cos, sin) of pos[n][axis(p)] * freq[p] for every token n and pair p.
@@ -58,6 +62,6 @@ hipError_t launch_rope_table(const int32_t* pos, const double* freq, float2* tab
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream);
 // Exact merge of split partials: O = sum_i 2^(m_i - m) O_i / sum_i 2^(m_i - m) l_i.
 hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream);
-hipError_t launch_attn_fp8(const Fp8Args& a, int head_dim, hipStream_t stream);
+hipError_t launch_attn_fp8(const Fp8Args& a, int head_dim, const Schedule& sch, hipStream_t stream);
 
 }  // namespace flux
