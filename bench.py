@@ -46,7 +46,8 @@ def source_sha(kernel):
     if not os.path.exists(p):
         return None
     h = hashlib.sha256()
-    for f in (p, os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc", "device_common.h")):
+    csrc = os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc")
+    for f in (p, os.path.join(csrc, "attn_common.h"), os.path.join(csrc, "device_common.h")):
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
