@@ -144,7 +144,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   f32x16 o[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) o[db] = (f32x16){};
-  float m_ref = 0.f;   // running max of c*score, exp2 domain, bf16-representable
+  float m_ref = 0.f;   // reference max of c*score, exp2 domain, bf16-representable
   float lsum = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int grp = lane >> 4, li = lane & 15;
@@ -170,41 +170,39 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
       if (key >= N) s[e] = -INFINITY;
     }
   };
-  // Block max and lazy update of the running max (in the exp2 domain).  Returns
-  // whether any lane of the wave moved its reference; *alpha is the factor by
-  // which earlier partial results must be scaled (1 where nothing moved).
-  // s holds c*score - m_ref.  The first block of a range always sets m_ref to
-  // its (bf16-rounded) max; later blocks move it only when a row exceeds it
-  // by more than 8.  When it moves, s is re-based on the new m_ref and *alpha
-  // is the factor for everything accumulated so far (0 on the first block,
-  // where nothing has been).
-  auto update_max = [&](f32x16& s, bool first, float* alpha) -> bool {
+  // Running reference m (exp2 domain, bf16-representable; s holds
+  // c*score - m through the folded MFMA column).  The first block of a K/V range
+  // sets m to its row max.  Later blocks do not look at the max: p = exp2(s) is
+  // formed directly and the block's row sum checked afterwards.  Only when a
+  // row's block sum reaches 2^32 (or is not finite) does the rare path move m up
+  // to the block max, rescale O, l and the pending score blocks, and recompute
+  // P.  Between moves p <= 2^32, so O and l stay far inside the fp32 range; the
+  // result is the same softmax.
+  auto rebase = [&](float m_new, f32x16& s) {
+    const float shift = m_ref - m_new;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] += shift;
+  };
+  auto set_ref = [&](float m_new) {
+    m_ref = m_new;
+    if (g == 0) qm[0] = (__bf16)(-m_new);
+  };
+  auto block_max = [&](const f32x16& s) -> float {
     float mt = s[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
-    mt = fmaxf(mt, swap_halves(mt));
-    const bool need = first || mt > 8.0f;
-    *alpha = 1.0f;
-    if (__ballot(need) == 0) return false;
-    const float m_new = need ? bf16_round(m_ref + mt) : m_ref;
-    const float shift = m_ref - m_new;
-    *alpha = first ? 0.0f : __builtin_amdgcn_exp2f(shift);
-    m_ref = m_new;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] += shift;
-    if (g == 0) qm[0] = (__bf16)(-m_new);
-    return true;
+    return fmaxf(mt, swap_halves(mt));
   };
   auto rescale_o = [&](float alpha) {
     lsum *= alpha;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
   };
-  // P^T fragment of one 16-key slice (hh) of block s; row sums over the
-  // bf16-rounded values.  The dot operand is built as a bf16x2 directly: a
-  // bit-cast vector element here made the compiler feed one register to every
-  // dot instruction.
-  auto make_p = [&](const f32x16& s, int hh) -> u32x4 {
+  // P^T fragment of one 16-key slice (hh) of block s; the row sum of the
+  // bf16-rounded values goes to bsum.  The dot operand is built as a bf16x2
+  // directly: a bit-cast vector element here made the compiler feed one
+  // register to every dot instruction.
+  auto make_p = [&](const f32x16& s, int hh, float& bsum) -> u32x4 {
     u32x4 pf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -214,16 +212,11 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
       pp[0] = (__bf16)p0;
       pp[1] = (__bf16)p1;
       pf[i] = __builtin_bit_cast(uint32_t, pp);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+      bsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, bsum, false);
     }
     return pf;
   };
-  // Multiply a packed bf16 P^T fragment by alpha (rare: the running max moved
-  // after it was formed).
-  auto scale_p = [&](u32x4& pf, float alpha) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pf[i] = pack_bf16(bf16lo(pf[i]) * alpha, bf16hi(pf[i]) * alpha);
-  };
+  auto block_ok = [&](float bsum) -> bool { return __ballot(!(bsum < 0x1p32f)) == 0; };
   // O^T += V^T P^T for the 16-key slice (kb, hh).
   auto pv = [&](const FLUX_LDS char* vl, int kb, int hh, const u32x4& pf) {
     const int krow0 = 32 * kb + 16 * hh + 8 * (grp >> 1) + (li >> 2);
@@ -253,8 +246,8 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   //   4. O += PV(block 0, keys 16-31)  || P(block 1, keys 16-31)
   //   5. O += PV(block 1)              || RoPE + store of the other half of tile j+1;
   //                                      its loads for tile j+2
-  // The running max is checked per 32-key block; when it moves (rare after
-  // the first tile) the already packed P of block 0 is rescaled as well.
+  // No max reduction sits between a score block and its P: the block row
+  // sums are checked after P is formed (see make_p / block_ok).
   // One tile step; LAST selects the masked variant for a ragged final tile.
   auto tile_step = [&](int j, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
@@ -262,7 +255,6 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[buf];
     const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[buf];
     const int kt0 = j * C::BN;
-    float alpha;
 
     // 1. S0 = QK(block 0) || RoPE + store of the first half of tile j+1.
     f32x16 s0 = qk(kl, 0);
@@ -270,28 +262,49 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int p = 0; p < HALF; ++p) stage_store(buf ^ 1, p);
     sched_interleave<C::KSTEPS, 4>();
     if (LAST) mask(kt0, 0, s0);
-    if (update_max(s0, j == kv0, &alpha)) rescale_o(alpha);
+    if (j == kv0) {  // first block of the range: m = its row max
+      const float m_new = bf16_round(m_ref + block_max(s0));
+      rebase(m_new, s0);
+      set_ref(m_new);
+    }
 
     // 2. S1 = QK(block 1) || P of block 0; loads of the first half of tile j+2.
     f32x16 s1 = qk(kl, 1);
-    u32x4 p00 = make_p(s0, 0);
-    u32x4 p01 = make_p(s0, 1);
+    float b0 = 0.f, b1 = 0.f;
+    u32x4 p00 = make_p(s0, 0, b0);
+    u32x4 p01 = make_p(s0, 1, b0);
 #pragma unroll
     for (int p = 0; p < HALF; ++p) stage_load((j + 2) * C::BN, p);
     sched_interleave<C::KSTEPS, 6>();
     if (LAST) mask(kt0, 1, s1);
-    if (update_max(s1, false, &alpha)) {
-      rescale_o(alpha);
-      scale_p(p00, alpha);
-      scale_p(p01, alpha);
+    if (!block_ok(b0)) {  // rare: move m up to block 0's max (s1 used the old m too)
+      const float m_new = fmaxf(m_ref, bf16_round(m_ref + block_max(s0)));
+      rescale_o(__builtin_amdgcn_exp2f(m_ref - m_new));
+      rebase(m_new, s0);
+      rebase(m_new, s1);
+      set_ref(m_new);
+      b0 = 0.f;
+      p00 = make_p(s0, 0, b0);
+      p01 = make_p(s0, 1, b0);
     }
+    lsum += b0;
 
     // 3.-5. O += PV(block 0) || P of block 1; O += PV(block 1) || RoPE + store
     // of the second half of tile j+1 and its loads for tile j+2.
     pv(vl, 0, 0, p00);
-    u32x4 p10 = make_p(s1, 0);
+    u32x4 p10 = make_p(s1, 0, b1);
     pv(vl, 0, 1, p01);
-    u32x4 p11 = make_p(s1, 1);
+    u32x4 p11 = make_p(s1, 1, b1);
+    if (!block_ok(b1)) {  // rare: O already holds PV(block 0) at the old m
+      const float m_new = fmaxf(m_ref, bf16_round(m_ref + block_max(s1)));
+      rescale_o(__builtin_amdgcn_exp2f(m_ref - m_new));
+      rebase(m_new, s1);
+      set_ref(m_new);
+      b1 = 0.f;
+      p10 = make_p(s1, 0, b1);
+      p11 = make_p(s1, 1, b1);
+    }
+    lsum += b1;
     pv(vl, 1, 0, p10);
     pv(vl, 1, 1, p11);
 #pragma unroll
