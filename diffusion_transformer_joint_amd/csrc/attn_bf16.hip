@@ -9,19 +9,24 @@
 // works: rotary embeddings fused into the surrounding kernels).
 //
 // Work decomposition
-//   workgroup = 8 waves x 32 query rows = 256 rows (two waves per SIMD, so one
-//   wave's softmax can run while the other issues MFMAs); K/V streamed in
-//   64-key tiles, double-buffered in LDS (K rotated on the way in, rows padded).
+//   workgroup = 8 waves x 32 query rows = 256 rows (two waves per SIMD); K/V
+//   streamed in 64-key tiles, double-buffered in LDS (K rotated on the way
+//   in, rows padded).
 //   S^T = K Q^T is computed so that each lane owns one query (lane % 32) and
 //   16 keys per 32-key block: the softmax row reductions are in-lane plus one
 //   exchange between the two wave halves.
 //   O^T += V^T P^T reuses the S^T accumulator registers directly as the P^T
 //   operand (rounded to bf16); V^T fragments come from row-major V in LDS
 //   through the gfx950 transpose read.
-//   Online softmax (Milakov & Gimelshein 2018) with a lazily updated running
-//   max: the reference max only moves when a row's tile max exceeds it by more
-//   than 2^8 in the exp2 domain, which keeps every p <= 256 and skips most
-//   rescales of the output accumulators; the result is the same softmax.
+//   Software pipeline over tiles: iteration t issues one fixed-order stream of
+//   MFMAs, S(t) = QK(t) then O += PV(t-1), and places the independent VALU
+//   work between them (RoPE and LDS stores of the next tiles beside QK, P(t)
+//   beside PV), so that each wave keeps its own matrix unit busy while it
+//   computes the softmax.
+//   Online softmax (Milakov & Gimelshein 2018) against a reference max that
+//   rarely moves: the first tile of a K/V range sets it to the row max; later
+//   tiles form p = exp2(c s - m) directly and only move m (rescaling O and l)
+//   when a row's tile sum reaches 2^32.  The result is the same softmax.
 //
 // Layouts: q, k, v, o [B][N][H][D] bf16; rope [N][D/2] float2 (cos, sin).
 #include "attn_common.h"
@@ -106,7 +111,6 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   // as soon as the matching half of tile j+1 has been written to LDS.
   const int st_chunk = tid % C::CPR;
   const int st_row0 = tid / C::CPR;
-  constexpr int HALF = C::NPASS / 2;
   u32x4 kraw[C::NPASS], vraw[C::NPASS];
   f32x4 kcs[C::NPASS][2];
   // Buffer loads relative to the tile's first row: rows at or past N read as
@@ -121,24 +125,37 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     kv_off[p] = (uint32_t)(r * tok_stride * 2 + st_chunk * 16);
     rp_off[p] = (uint32_t)(r * (D / 2) * 8 + st_chunk * 32);
   }
-  auto stage_load = [&](int kt0, int p) {
+  auto tile_bytes = [&](int kt0) -> uint32_t {
     const int rows = N - kt0;
-    const uint32_t kv_bytes = rows > 0 ? (uint32_t)((rows - 1) * tok_stride * 2 + 2 * D) : 0u;
-    const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 8) : 0u;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, kv_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)kt0 * tok_stride, kv_bytes);
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rope + (size_t)kt0 * (D / 2), rp_bytes);
-    kraw[p] = buffer_load_b128(rk, kv_off[p]);
-    vraw[p] = buffer_load_b128(rv, kv_off[p]);
-    kcs[p][0] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off[p]));
-    kcs[p][1] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off[p] + 16));
+    return rows > 0 ? (uint32_t)((rows - 1) * tok_stride * 2 + 2 * D) : 0u;
   };
-  auto stage_store = [&](int buf, int p) {
+  auto load_k = [&](int kt0) {
+    const int rows = N - kt0;
+    const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 8) : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, tile_bytes(kt0));
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rope + (size_t)kt0 * (D / 2), rp_bytes);
+#pragma unroll
+    for (int p = 0; p < C::NPASS; ++p) {
+      kraw[p] = buffer_load_b128(rk, kv_off[p]);
+      kcs[p][0] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off[p]));
+      kcs[p][1] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off[p] + 16));
+    }
+  };
+  auto load_v = [&](int kt0) {
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)kt0 * tok_stride, tile_bytes(kt0));
+#pragma unroll
+    for (int p = 0; p < C::NPASS; ++p) vraw[p] = buffer_load_b128(rv, kv_off[p]);
+  };
+  auto store_k = [&](int buf) {
     FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
+#pragma unroll
+    for (int p = 0; p < C::NPASS; ++p)
+      lds_write_b128(kl + k_off<D>(st_row0 + p * C::RPP, st_chunk), rope_chunk(kraw[p], kcs[p][0], kcs[p][1]));
+  };
+  auto store_v = [&](int buf) {
     FLUX_LDS char* vl = (FLUX_LDS char*)vsm[buf];
-    const int r = st_row0 + p * C::RPP;
-    lds_write_b128(kl + k_off<D>(r, st_chunk), rope_chunk(kraw[p], kcs[p][0], kcs[p][1]));
-    lds_write_b128(vl + v_off<D>(r, st_chunk), vraw[p]);
+#pragma unroll
+    for (int p = 0; p < C::NPASS; ++p) lds_write_b128(vl + v_off<D>(st_row0 + p * C::RPP, st_chunk), vraw[p]);
   };
 
   f32x16 o[C::DB];
@@ -231,93 +248,193 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     }
   };
 
-#pragma unroll
-  for (int p = 0; p < C::NPASS; ++p) stage_load(kv0 * C::BN, p);
-#pragma unroll
-  for (int p = 0; p < C::NPASS; ++p) stage_store(0, p);
-#pragma unroll
-  for (int p = 0; p < C::NPASS; ++p) stage_load((kv0 + 1) * C::BN, p);
+  // Software pipeline over 64-key tiles.  Iteration t:
+  //   MFMA:  S(t) = QK(t) (both 32-key blocks), then O += PV(t-1) with P(t-1)
+  //          from the previous iteration;
+  //   VALU:  P(t) = exp2(S(t)) with its row sums, beside the wave's own PV
+  //          MFMAs; RoPE + LDS store of K(t+1) and store of V(t) beside QK;
+  //          global loads of K(t+2) and V(t+1).
+  //   barrier.
+  // K(t) is read in iteration t and V(t) in iteration t+1, so K(t+1) and V(t)
+  // are written into the buffers that K(t-1) and V(t-2) held: two buffers each.
+  load_k(kv0 * C::BN);
+  store_k(0);
+  load_k((kv0 + 1) * C::BN);
+  load_v(kv0 * C::BN);
   __syncthreads();
 
-  // Per tile j (buffer j&1 holds tile j, buffer (j+1)&1 receives tile j+1):
-  //   1. S0 = QK(block 0)              || RoPE + LDS store of half of tile j+1
-  //   2. S1 = QK(block 1)              || P(block 0); loads of that half of tile j+2
-  //   3. O += PV(block 0, keys 0-15)   || P(block 1, keys 0-15)
-  //   4. O += PV(block 0, keys 16-31)  || P(block 1, keys 16-31)
-  //   5. O += PV(block 1)              || RoPE + store of the other half of tile j+1;
-  //                                      its loads for tile j+2
-  // No max reduction sits between a score block and its P: the block row
-  // sums are checked after P is formed (see make_p / block_ok).
-  // One tile step; LAST selects the masked variant for a ragged final tile.
-  auto tile_step = [&](int j, auto last_tag) {
+  u32x4 pp[4];  // P(t-1): fragments (block 0, keys 0-15), (0, 16-31), (1, 0-15), (1, 16-31)
+  // The first tile of the range (no PV yet): its row max sets m.
+  auto step_first = [&](auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
-    const int buf = (j - kv0) & 1;
-    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[buf];
-    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[buf];
-    const int kt0 = j * C::BN;
+    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[0];
+    const int kt0 = kv0 * C::BN;
 
-    // 1. S0 = QK(block 0) || RoPE + store of the first half of tile j+1.
     f32x16 s0 = qk(kl, 0);
-#pragma unroll
-    for (int p = 0; p < HALF; ++p) stage_store(buf ^ 1, p);
-    sched_interleave<C::KSTEPS, 4>();
-    if (LAST) mask(kt0, 0, s0);
-    if (j == kv0) {  // first block of the range: m = its row max
-      const float m_new = bf16_round(m_ref + block_max(s0));
-      rebase(m_new, s0);
-      set_ref(m_new);
-    }
-
-    // 2. S1 = QK(block 1) || P of block 0; loads of the first half of tile j+2.
     f32x16 s1 = qk(kl, 1);
-    float b0 = 0.f, b1 = 0.f;
-    u32x4 p00 = make_p(s0, 0, b0);
-    u32x4 p01 = make_p(s0, 1, b0);
-#pragma unroll
-    for (int p = 0; p < HALF; ++p) stage_load((j + 2) * C::BN, p);
-    sched_interleave<C::KSTEPS, 6>();
-    if (LAST) mask(kt0, 1, s1);
-    if (!block_ok(b0)) {  // rare: move m up to block 0's max (s1 used the old m too)
-      const float m_new = fmaxf(m_ref, bf16_round(m_ref + block_max(s0)));
+    if (LAST) {
+      mask(kt0, 0, s0);
+      mask(kt0, 1, s1);
+    }
+    {
+      const float m_new = bf16_round(m_ref + fmaxf(block_max(s0), block_max(s1)));
+      rebase(m_new, s0);
+      rebase(m_new, s1);
+      set_ref(m_new);
+    }
+    float b = 0.f;
+    pp[0] = make_p(s0, 0, b);
+    pp[1] = make_p(s0, 1, b);
+    pp[2] = make_p(s1, 0, b);
+    pp[3] = make_p(s1, 1, b);
+    if (!block_ok(b)) {  // rare: move m up to this tile's max
+      const float m_new = fmaxf(m_ref, bf16_round(m_ref + fmaxf(block_max(s0), block_max(s1))));
       rescale_o(__builtin_amdgcn_exp2f(m_ref - m_new));
       rebase(m_new, s0);
       rebase(m_new, s1);
       set_ref(m_new);
-      b0 = 0.f;
-      p00 = make_p(s0, 0, b0);
-      p01 = make_p(s0, 1, b0);
+      b = 0.f;
+      pp[0] = make_p(s0, 0, b);
+      pp[1] = make_p(s0, 1, b);
+      pp[2] = make_p(s1, 0, b);
+      pp[3] = make_p(s1, 1, b);
     }
-    lsum += b0;
+    lsum += b;
+    store_k(1);
+    store_v(0);
+    load_k((kv0 + 2) * C::BN);
+    load_v((kv0 + 1) * C::BN);
+    __syncthreads();
+  };
 
-    // 3.-5. O += PV(block 0) || P of block 1; O += PV(block 1) || RoPE + store
-    // of the second half of tile j+1 and its loads for tile j+2.
-    pv(vl, 0, 0, p00);
-    u32x4 p10 = make_p(s1, 0, b1);
-    pv(vl, 0, 1, p01);
-    u32x4 p11 = make_p(s1, 1, b1);
-    if (!block_ok(b1)) {  // rare: O already holds PV(block 0) at the old m
-      const float m_new = fmaxf(m_ref, bf16_round(m_ref + block_max(s1)));
+  // Every tile after the first of the range: one MFMA stream (S(t) = QK(t),
+  // then O += PV(t-1)) in a fixed order, each MFMA followed by the LDS operand
+  // read NPF MFMAs ahead and a slice of independent VALU work: RoPE + store of
+  // K(t+1) and store of V(t) beside QK, P(t) beside PV once the P(t-1)
+  // fragment it replaces has been consumed.
+  auto rope_pair = [&](uint32_t x, float cc, float ss) -> uint32_t {
+    const float x0 = bf16lo(x), x1 = bf16hi(x);
+    return pack_bf16(x0 * cc - x1 * ss, x0 * ss + x1 * cc);
+  };
+  auto p_pair = [&](float x0, float x1, float& bsum) -> uint32_t {
+    bf16x2 q2;
+    q2[0] = (__bf16)__builtin_amdgcn_exp2f(x0);
+    q2[1] = (__bf16)__builtin_amdgcn_exp2f(x1);
+    bsum = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, bsum, false);
+    return __builtin_bit_cast(uint32_t, q2);
+  };
+  auto step_main = [&](int t, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const int i = t - kv0;
+    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[i & 1];
+    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[(i + 1) & 1];  // V(t-1)
+    FLUX_LDS char* kw = (FLUX_LDS char*)ksm[(i + 1) & 1];              // K(t+1)
+    FLUX_LDS char* vw = (FLUX_LDS char*)vsm[i & 1];                    // V(t)
+    const int kt0 = t * C::BN;
+    // MFMA j < NK: S(t), K fragment j; NK <= j < NL: PV(t-1), V fragment j - NK.
+    constexpr int NK = 2 * C::KSTEPS, NL = NK + 4 * C::DB;
+    auto ld = [&](int j) -> u32x4 {
+      if (j < NK) {
+        const int kb = j / C::KSTEPS, tt = j % C::KSTEPS;
+        return lds_read_b128(kl + k_off<D>(32 * kb + krow_perm(l32), 2 * tt + g));
+      }
+      const int v = j - NK, kb = v / (2 * C::DB), hh = (v / C::DB) & 1, db = v % C::DB;
+      const int krow0 = 32 * kb + 16 * hh + 8 * (grp >> 1) + (li >> 2);
+      const int d = 32 * db + 16 * (grp & 1) + 4 * (li & 3);
+      const u32x2 lo = lds_read_tr16(vl + v_off<D>(krow0, d >> 3) + (d & 7) * 2);
+      const u32x2 hi = lds_read_tr16(vl + v_off<D>(krow0 + 4, d >> 3) + (d & 7) * 2);
+      return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+    };
+    // Slot plan (slot j follows MFMA j): RoPE of the 4 * NPASS pairs of K(t+1)
+    // in every other slot from 0, store of V(t) in slots 1 and 3, loads of
+    // V(t+1) in slot 5 and of K(t+2) once its registers are free; P(t) slice q
+    // in the four slots after P(t-1) slice q has been consumed (the last slice
+    // after the stream).
+    constexpr int NPF = 3;                           // operand reads ahead
+    constexpr int ROPE_END = 2 * 4 * C::NPASS;       // slots 0, 2, .., ROPE_END - 2
+    constexpr int VST0 = 1, VST1 = 3, LVS = 5, LKS = ROPE_END > NK ? ROPE_END : NK;
+    u32x4 fb[NPF];
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) fb[j] = ld(j);
+    f32x16 s0 = mfma_bf16(kone, qm, (f32x16){}), s1 = (f32x16){};
+    u32x4 kr[C::NPASS];
+    float b = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NL>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const u32x4 x = fb[j % NPF];
+      if constexpr (j + NPF < NL) fb[j % NPF] = ld(j + NPF);
+      if constexpr (j < C::KSTEPS) {
+        s0 = mfma_bf16(__builtin_bit_cast(bf16x8, x), qf[j], s0);
+        if constexpr (j == C::KSTEPS - 1) s1 = mfma_bf16(kone, qm, (f32x16){});
+      } else if constexpr (j < NK) {
+        s1 = mfma_bf16(__builtin_bit_cast(bf16x8, x), qf[j - C::KSTEPS], s1);
+      } else {
+        constexpr int v = j - NK, q4 = v / C::DB, db = v % C::DB;
+        o[db] = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, pp[q4]), o[db]);
+      }
+      if constexpr (j < ROPE_END && j % 2 == 0) {  // RoPE of K(t+1), one pair
+        constexpr int p = (j / 2) >> 2, e = (j / 2) & 3;
+        const f32x4 cs = kcs[p][e >> 1];
+        kr[p][e] = rope_pair(kraw[p][e], cs[2 * (e & 1)], cs[2 * (e & 1) + 1]);
+        if constexpr (e == 3) lds_write_b128(kw + k_off<D>(st_row0 + p * C::RPP, st_chunk), kr[p]);
+      }
+      if constexpr (j == VST0 || j == VST1) {     // V(t)
+        constexpr int p = j == VST0 ? 0 : 1;
+        lds_write_b128(vw + v_off<D>(st_row0 + p * C::RPP, st_chunk), vraw[p]);
+      }
+      if constexpr (j == LVS) load_v((t + 1) * C::BN);
+      if constexpr (j == LKS) load_k((t + 2) * C::BN);
+      if constexpr (j >= NK) {
+        constexpr int v = j - NK;
+        if (LAST && v == 0) mask(kt0, 0, s0);
+        if (LAST && v == 2) mask(kt0, 1, s1);
+        if constexpr (v >= C::DB) {                 // P(t) slice q replaces P(t-1) slice q
+          constexpr int q = (v - C::DB) / C::DB, e = (v - C::DB) % C::DB;
+          const f32x16& sq = q < 2 ? s0 : s1;
+          constexpr int hh = q & 1;
+#pragma unroll
+          for (int ee = 0; ee < 4 / C::DB; ++ee) {
+            const int e2 = e * (4 / C::DB) + ee;
+            pp[q][e2] = p_pair(sq[8 * hh + 2 * e2], sq[8 * hh + 2 * e2 + 1], b);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) pp[3][e2] = p_pair(s1[8 + 2 * e2], s1[8 + 2 * e2 + 1], b);
+    if (!block_ok(b)) {  // rare: move m up to this tile's max
+      const float m_new = fmaxf(m_ref, bf16_round(m_ref + fmaxf(block_max(s0), block_max(s1))));
       rescale_o(__builtin_amdgcn_exp2f(m_ref - m_new));
+      rebase(m_new, s0);
       rebase(m_new, s1);
       set_ref(m_new);
-      b1 = 0.f;
-      p10 = make_p(s1, 0, b1);
-      p11 = make_p(s1, 1, b1);
+      b = 0.f;
+      pp[0] = make_p(s0, 0, b);
+      pp[1] = make_p(s0, 1, b);
+      pp[2] = make_p(s1, 0, b);
+      pp[3] = make_p(s1, 1, b);
     }
-    lsum += b1;
-    pv(vl, 1, 0, p10);
-    pv(vl, 1, 1, p11);
-#pragma unroll
-    for (int p = HALF; p < C::NPASS; ++p) stage_store(buf ^ 1, p);
-#pragma unroll
-    for (int p = HALF; p < C::NPASS; ++p) stage_load((j + 2) * C::BN, p);
-    sched_interleave<4 * C::DB, 5>();
+    lsum += b;
     __syncthreads();
   };
 
   const int full_end = min(kv1, N / C::BN);  // tiles before this one are full
-  for (int j = kv0; j < full_end; ++j) tile_step(j, std::false_type{});
-  if (full_end < kv1) tile_step(full_end, std::true_type{});
+  if (kv0 < full_end) {
+    step_first(std::false_type{});
+    for (int t = kv0 + 1; t < full_end; ++t) step_main(t, std::false_type{});
+    if (full_end < kv1) step_main(full_end, std::true_type{});
+  } else {
+    step_first(std::true_type{});
+  }
+  {
+    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[(kv1 - 1 - kv0) & 1];
+    pv(vl, 0, 0, pp[0]);
+    pv(vl, 0, 1, pp[1]);
+    pv(vl, 1, 0, pp[2]);
+    pv(vl, 1, 1, pp[3]);
+  }
 
   // ---- epilogue.  A K/V range of a split tile stores its fp32 partial state.
   const float ltot = lsum + swap_halves(lsum);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace flux {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -79,6 +81,16 @@ __device__ __forceinline__ uint32_t buffer_load_b32(__amdgpu_buffer_rsrc_t r, ui
 
 __device__ __forceinline__ float bf16_round(float x) {
   return (float)(__bf16)x;
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 in order: a loop
+// that is unrolled however large its body is, with a compile-time index.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Value of lane l ^ 32 (the other half of the wave).
