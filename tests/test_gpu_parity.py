@@ -77,6 +77,44 @@ def test_peaked_scores_exercise_rescaling():
     assert_close(out_fp64(run_hip(inp)), ref, tol, "sigma 2")
 
 
+def _bf16_bits(x):
+    return I.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_scores_far_below_zero():
+    # RoPE off (all-zero positions), Q = 4 * ones and K = -4 * ones: every
+    # scaled score is -2048 / sqrt(128) (about -261 in the exp2 domain), far
+    # below where exp2 underflows, and all scores are equal, so O is the mean
+    # of V.  A reference max that stayed at zero would give 0 / 0 here.
+    import dataclasses
+    w = custom("neg", 1, 128, [S("text", 2048)], sigma=1.0)
+    inp = I.make_inputs(w)
+    q = np.broadcast_to(_bf16_bits(4.0), inp.q.shape).copy()
+    k = np.broadcast_to(_bf16_bits(-4.0), inp.k.shape).copy()
+    inp = dataclasses.replace(inp, q=q, k=k)
+    pos = np.zeros_like(inp.pos)
+    got = out_fp64(run_hip(inp, pos=pos))
+    assert_close(got, ref_full(inp, pos=pos), BF16_TOL, "scores ~ -261 (exp2 domain)")
+
+
+def test_reference_moves_down_then_up():
+    # RoPE off.  The first 256 keys score about -261 (exp2 domain) against
+    # every query, the others about +16: the row total of the first tiles
+    # underflows (the reference moves down to their max), then the later tiles
+    # overflow that reference (it moves up again).  Oracle: exact softmax.
+    import dataclasses
+    w = custom("updown", 1, 128, [S("text", 2048)], sigma=1.0)
+    inp = I.make_inputs(w)
+    q = np.broadcast_to(_bf16_bits(4.0), inp.q.shape).copy()
+    k = np.broadcast_to(_bf16_bits(0.25), inp.k.shape).copy()
+    k[:, :256] = _bf16_bits(-4.0)
+    inp = dataclasses.replace(inp, q=q, k=k)
+    pos = np.zeros_like(inp.pos)
+    ref = ref_full(inp, pos=pos)
+    got = out_fp64(run_hip(inp, pos=pos))
+    assert_close(got, ref, BF16_TOL, "scores -261 then +16 (exp2 domain)")
+
+
 def test_translation_invariance():
     w = custom("transl", 2, 128, [S("text", 64), S("image", 16, 16)])
     inp = I.make_inputs(w)
