@@ -8,9 +8,11 @@ the RoPE angle table plus the joint attention kernel (RoPE fused into its Q/K
 loads, online softmax, bf16 MFMA), through the C ABI.  The timed workload is the
 1024^2 single-reference edit call: 512 text + 4,096 image + 4,096 reference
 tokens (8,704), 24 heads, head_dim 128, bf16 Q/K/V ~ N(0, 0.25).  Inputs are
-resident in HBM before timing starts.  The 4,608-token text-to-image call and the
-66,048-token e4m3 call (and, with --all, the 25,088-token call) are reported as
-extra fields of the same JSON line.
+resident in HBM before timing starts.  The 4,608-token text-to-image call, the
+66,048-token e4m3 call, the edit call in segment-local mode (each segment
+attending to itself), one GPU's share of the edit call under 8-way head
+sharding (3 heads, split K/V schedule) and, with --all, the 25,088-token call
+are reported as extra fields of the same JSON line.
 
 Rank 0 prints one JSON line.  Only one GPU is supported: the path shards over
 heads with no communication inside the kernel, and this build measures one
@@ -70,12 +72,12 @@ def recorded_traffic(kernel, workload):
         return None
 
 
-def measure(workload, steps, warmup):
+def measure(workload, steps, warmup, mode="joint"):
     import torch
     from diffusion_transformer_joint_amd import inputs as I
     from diffusion_transformer_joint_amd.flux_attn import Plan
 
-    w = I.WORKLOADS[workload]
+    w = I.WORKLOADS[workload] if isinstance(workload, str) else workload
     inp = I.make_inputs(w)
     dev = torch.device("cuda:0")
     if inp.scales is None:
@@ -90,7 +92,7 @@ def measure(workload, steps, warmup):
     plan = Plan(w.batch, w.heads, w.head_dim, w.tokens, dtype="fp8" if w.fp8 else "bf16")
     segs = w.segment_tokens
     for _ in range(warmup):
-        plan.forward(q, k, v, segs, pos, out=out, scales=sc)
+        plan.forward(q, k, v, segs, pos, out=out, scales=sc, mode=mode)
     torch.cuda.synchronize()
     plan.timing_enable(steps)
     stream = torch.cuda.current_stream()
@@ -99,17 +101,20 @@ def measure(workload, steps, warmup):
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(steps):
-        plan.forward(q, k, v, segs, pos, out=out, scales=sc)
+        plan.forward(q, k, v, segs, pos, out=out, scales=sc, mode=mode)
     e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kernel_ms = plan.timing_read()
     plan.close()
     step_ms = e0.elapsed_time(e1) / steps
-    flops = w.flops()
+    if mode == "joint":
+        flops = w.flops()
+    else:  # each segment attends to itself
+        flops = 4.0 * w.batch * w.heads * w.head_dim * sum(n * n for n in segs)
     kavg = sum(kernel_ms) / len(kernel_ms)
     return {
-        "workload": w.name, "tokens": w.tokens, "heads": w.heads, "head_dim": w.head_dim, "batch": w.batch,
+        "workload": w.name if mode == "joint" else f"{w.name} ({mode})", "mode": mode, "tokens": w.tokens, "heads": w.heads, "head_dim": w.head_dim, "batch": w.batch,
         "dtype": "fp8_e4m3" if w.fp8 else "bf16", "flops": flops,
         "ms_per_step": step_ms, "wall_ms_per_step": (t1 - t0) * 1e3 / steps,
         "kernel_ms_avg": kavg, "kernel_ms_min": min(kernel_ms),
@@ -182,19 +187,24 @@ def main():
     main_run = measure(args.workload, args.steps, args.warmup)
     log(f"{args.workload}: {main_run['kernel_tflops']:.1f} TFLOP/s kernel, {main_run['ms_per_step']:.3f} ms/step")
     extra = []
-    others = ["t2i1024", "gen4k_fp8"] + (["gen2048r2"] if args.all else [])
-    for name in others:
-        if name == args.workload:
+    import dataclasses
+    from diffusion_transformer_joint_amd import inputs as I
+    share = dataclasses.replace(I.WORKLOADS["edit1024"], heads=3, name="edit1024_3heads",
+                                description="one GPU's share (3 of 24 heads) of the 8,704-token edit call")
+    others = [("t2i1024", "joint"), ("gen4k_fp8", "joint"), ("edit1024", "segment_local"), (share, "joint")] + \
+        ([("gen2048r2", "joint")] if args.all else [])
+    for name, mode in others:
+        if name == args.workload and mode == "joint":
             continue
         r = measure(name, max(5, args.steps // 5) if name == "gen4k_fp8" else max(5, args.steps // 2),
-                    max(2, args.warmup // 2))
+                    max(2, args.warmup // 2), mode=mode)
         r["frac_bf16_peak"] = r["kernel_tflops"] / BF16_PEAK
         if r["dtype"] != "bf16":
             # QK^T runs at the fp8 rate, PV at the bf16 rate (P is kept in bf16)
             r["frac_fp8_peak"] = r["kernel_tflops"] / FP8_PEAK
             r["frac_mixed_ceiling"] = r["kernel_tflops"] / (2.0 / (1.0 / FP8_PEAK + 1.0 / BF16_PEAK))
         extra.append(r)
-        log(f"{name}: {r['kernel_tflops']:.1f} TFLOP/s kernel")
+        log(f"{r['workload']}: {r['kernel_tflops']:.1f} TFLOP/s kernel")
 
     kernel = "attn_bf16"
     traffic = recorded_traffic(kernel, args.workload)

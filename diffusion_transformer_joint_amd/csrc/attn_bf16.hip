@@ -76,9 +76,10 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const size_t tok_stride = (size_t)H * D;  // elements between consecutive tokens
-  const uint16_t* qbase = a.q + (size_t)b * N * tok_stride + (size_t)h * D;
-  const uint16_t* kbase = a.k + (size_t)b * N * tok_stride + (size_t)h * D;
-  const uint16_t* vbase = a.v + (size_t)b * N * tok_stride + (size_t)h * D;
+  const size_t bat = (size_t)b * a.batch_tokens * tok_stride;
+  const uint16_t* qbase = a.q + bat + (size_t)h * D;
+  const uint16_t* kbase = a.k + bat + (size_t)h * D;
+  const uint16_t* vbase = a.v + bat + (size_t)h * D;
   const float c = a.c;
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated, held in registers.
@@ -454,7 +455,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   // ---- epilogue: O = O^T / l, bf16, stored row-major.
   const float inv = 1.0f / ltot;
   if (qrow < N) {
-    uint16_t* orow = a.o + (size_t)b * N * tok_stride + (size_t)qrow * tok_stride + (size_t)h * D;
+    uint16_t* orow = a.o + bat + (size_t)qrow * tok_stride + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
   const size_t tok_stride = (size_t)a.heads * D;
-  *(u32x4*)(a.o + (size_t)b * a.n_tokens * tok_stride + (size_t)row * tok_stride + (size_t)h * D + d0) = out;
+  *(u32x4*)(a.o + (size_t)b * a.batch_tokens * tok_stride + (size_t)row * tok_stride + (size_t)h * D + d0) = out;
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream) {

@@ -112,9 +112,10 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const size_t tok_stride = (size_t)H * D;  // codes between consecutive tokens
-  const uint8_t* qbase = a.q + (size_t)b * N * tok_stride + (size_t)h * D;
-  const uint8_t* kbase = a.k + (size_t)b * N * tok_stride + (size_t)h * D;
-  const uint8_t* vbase = a.v + (size_t)b * N * tok_stride + (size_t)h * D;
+  const size_t bat = (size_t)b * a.batch_tokens * tok_stride;
+  const uint8_t* qbase = a.q + bat + (size_t)h * D;
+  const uint8_t* kbase = a.k + bat + (size_t)h * D;
+  const uint8_t* vbase = a.v + bat + (size_t)h * D;
   const float s_q = a.scales[(0 * a.batch + b) * H + h];
   const float s_k = a.scales[(1 * a.batch + b) * H + h];
   const float s_v = a.scales[(2 * a.batch + b) * H + h];
@@ -321,7 +322,7 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   }
   const float inv = s_v / ltot;
   if (qrow < N) {
-    uint16_t* orow = a.o + (size_t)b * N * tok_stride + (size_t)qrow * tok_stride + (size_t)h * D;
+    uint16_t* orow = a.o + (size_t)b * a.batch_tokens * tok_stride + (size_t)qrow * tok_stride + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll

@@ -273,59 +273,76 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev != plan->device)
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan was created on device %d, current device is %d", plan->device, dev);
-  if (mode != FLUX_ATTN_JOINT) return fail(FLUX_ATTN_UNSUPPORTED, "segment-local mode is not built yet");
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   e = flux::launch_rope_table(pos_ids, plan->freq, plan->rope_table, n, c.head_dim, c.rope_axes_dim[0],
                               c.rope_axes_dim[1], stream);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   const float scale = c.softmax_scale > 0.0f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
   const float log2e = 1.4426950408889634f;
-  const int tiles = c.batch * c.num_heads * ((n + 255) / 256);
-  const flux::Schedule sch = flux::plan_schedule(tiles, (n + 63) / 64, plan->num_cus, plan->max_pieces, c.head_dim);
-  // The merge only needs the output, sizes and the partial buffers.
-  flux::AttnArgs a{};
-  a.o = static_cast<uint16_t*>(out);
-  a.rope = plan->rope_table;
-  a.n_tokens = n;
-  a.heads = c.num_heads;
-  a.batch = c.batch;
-  a.c = scale * log2e;
-  a.part_o = plan->part_o;
-  a.part_ml = plan->part_ml;
+  // Token ranges attended over: the whole sequence (joint), or each non-empty
+  // segment on its own (segment-local).  One attention launch (+ merge) per
+  // range; the ranges run one after another on the stream and share the
+  // plan's partial-state workspace.
+  const bool joint = mode == FLUX_ATTN_JOINT;
+  const int n_ranges = joint ? 1 : num_segments;
+  int last = 0;  // last non-empty range
+  for (int r = 0; r < n_ranges; ++r)
+    if (joint || segment_tokens[r] > 0) last = r;
   const bool timed = plan->timing_used < (int)plan->ev_start.size();
   if (timed) {
     e = hipEventRecord(plan->ev_start[plan->timing_used], stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
-  if (c.dtype == FLUX_ATTN_FP8_E4M3) {
-    flux::Fp8Args f{};
-    f.q = static_cast<const uint8_t*>(q);
-    f.k = static_cast<const uint8_t*>(k);
-    f.v = static_cast<const uint8_t*>(v);
-    f.scales = qkv_scale;
-    f.o = a.o;
-    f.rope = a.rope;
-    f.n_tokens = n;
-    f.heads = c.num_heads;
-    f.batch = c.batch;
-    f.c = a.c;
-    f.part_o = a.part_o;
-    f.part_ml = a.part_ml;
-    e = flux::launch_attn_fp8(f, c.head_dim, sch, stream);
-  } else {
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    e = flux::launch_attn_bf16(a, c.head_dim, sch, stream);
+  const size_t tok = (size_t)c.num_heads * c.head_dim;  // elements per token
+  size_t off = 0;
+  for (int r = 0; r < n_ranges; off += joint ? 0 : (size_t)segment_tokens[r], ++r) {
+    const int len = joint ? n : segment_tokens[r];
+    if (len == 0) continue;
+    const int tiles = c.batch * c.num_heads * ((len + 255) / 256);
+    const flux::Schedule sch = flux::plan_schedule(tiles, (len + 63) / 64, plan->num_cus, plan->max_pieces, c.head_dim);
+    flux::AttnArgs a{};
+    a.o = static_cast<uint16_t*>(out) + off * tok;
+    a.rope = plan->rope_table + off * (c.head_dim / 2);
+    a.n_tokens = len;
+    a.batch_tokens = n;
+    a.heads = c.num_heads;
+    a.batch = c.batch;
+    a.c = scale * log2e;
+    a.part_o = plan->part_o;
+    a.part_ml = plan->part_ml;
+    if (c.dtype == FLUX_ATTN_FP8_E4M3) {
+      flux::Fp8Args f{};
+      f.q = static_cast<const uint8_t*>(q) + off * tok;
+      f.k = static_cast<const uint8_t*>(k) + off * tok;
+      f.v = static_cast<const uint8_t*>(v) + off * tok;
+      f.scales = qkv_scale;
+      f.o = a.o;
+      f.rope = a.rope;
+      f.n_tokens = len;
+      f.batch_tokens = n;
+      f.heads = c.num_heads;
+      f.batch = c.batch;
+      f.c = a.c;
+      f.part_o = a.part_o;
+      f.part_ml = a.part_ml;
+      e = flux::launch_attn_fp8(f, c.head_dim, sch, stream);
+    } else {
+      a.q = static_cast<const uint16_t*>(q) + off * tok;
+      a.k = static_cast<const uint16_t*>(k) + off * tok;
+      a.v = static_cast<const uint16_t*>(v) + off * tok;
+      e = flux::launch_attn_bf16(a, c.head_dim, sch, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    // The joint call's timing pair brackets its attention kernel alone; in
+    // segment-local mode it spans all ranges (merges between them included).
+    if (timed && r == last) {
+      e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+      ++plan->timing_used;
+    }
+    e = flux::launch_attn_merge(a, c.head_dim, sch, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (timed) {
-    e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    ++plan->timing_used;
-  }
-  e = flux::launch_attn_merge(a, c.head_dim, sch, stream);
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();
 }
 

@@ -11,7 +11,8 @@ struct AttnArgs {
   const uint16_t* v;
   uint16_t* o;            // [B][N][H][D] bf16 bits
   const float2* rope;     // [N][D/2] (cos, sin)
-  int n_tokens;
+  int n_tokens;           // tokens attended over (one segment in segment-local mode)
+  int batch_tokens;       // tokens between consecutive batch entries of q, k, v, o
   int heads;
   int batch;
   int q_tiles;            // filled by the launcher
@@ -45,6 +46,7 @@ struct Fp8Args {
   uint16_t* o;            // [B][N][H][D] bf16 bits
   const float2* rope;     // [N][D/2]
   int n_tokens;
+  int batch_tokens;
   int heads;
   int batch;
   int q_tiles;

@@ -103,8 +103,15 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out);
  * qkv_scale are device pointers owned by the caller and must stay valid until
  * the stream has passed this work; segment_tokens is a host array read before
  * the call returns.  N = sum(segment_tokens).  out is fully overwritten.
- * A plan runs one forward at a time (its workspace is shared between calls);
- * separate plans are independent.  Returns after launching. */
+ * mode FLUX_ATTN_JOINT: every token attends to all N tokens (the joint
+ * blocks).  mode FLUX_ATTN_SEGMENT_LOCAL: a token of segment s attends only to
+ * the tokens of segment s, i.e. the formula above with j restricted to the
+ * segment ("FLUX.3 Image Klein Brings 2-Second AI Image Generation to
+ * Diffusers", Summary: the separate-stream blocks before the joint ones); the
+ * RoPE angles still come from the tokens' own position ids, and empty
+ * segments are skipped.  A plan runs one forward at a time (its workspace is
+ * shared between calls and between the segments of one call); separate plans
+ * are independent.  Returns after launching. */
 int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const void* v,
                       const float* qkv_scale, const int32_t* segment_tokens,
                       int32_t num_segments, const int32_t* pos_ids, void* out,
@@ -113,7 +120,9 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
 /* Kernel timing.  flux_attn_timing_enable(plan, capacity) with capacity > 0
  * creates capacity pairs of HIP events (capacity <= 4096); every following
  * forward() records one pair around its attention kernel (none once all pairs
- * are used), on the stream that kernel runs on.  capacity = 0 releases them.
+ * are used), on the stream that kernel runs on.  In segment-local mode the
+ * pair spans the attention kernels of all segments (the small merge kernels
+ * between them included).  capacity = 0 releases them.
  * flux_attn_timing_read() waits for the last recorded pair, writes the
  * durations in milliseconds of up to max_count recorded launches to
  * attn_ms[0..*count-1] (host array) and starts over.  The caller must not
