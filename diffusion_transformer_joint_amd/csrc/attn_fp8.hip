@@ -75,6 +75,15 @@ __device__ __forceinline__ u32x4 rope16_e4m3(u32x4 x, const f32x4* cs) {
   return y;
 }
 
+// One dword of codes (two pairs) rotated by cs = (c0, s0, c1, s1), halved.
+__device__ __forceinline__ uint32_t rope_dword_e4m3(uint32_t x, f32x4 cs) {
+  float f[4];
+  e4m3x4_to_f32(x, f);
+  const float c0 = 0.5f * cs[0], s0 = 0.5f * cs[1];
+  const float c1 = 0.5f * cs[2], s1 = 0.5f * cs[3];
+  return f32x4_to_e4m3(f[0] * c0 - f[1] * s0, f[0] * s0 + f[1] * c0, f[2] * c1 - f[3] * s1, f[2] * s1 + f[3] * c1);
+}
+
 // 16 codes to 16 bf16 (exact): two 16-byte halves.
 __device__ __forceinline__ void e4m3x16_to_bf16(u32x4 x, u32x4* lo, u32x4* hi) {
 #pragma unroll
@@ -145,54 +154,48 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   }
 
   // ---- staging: one 16-code chunk of K and of V per thread and tile.
-  const bool st_on = tid < C::NCH;
+  const bool st_on = C::NCH >= C::NT || tid < C::NCH;  // every thread stages when D = 128
   const int st_row = tid / C::CPR8, st_c = tid % C::CPR8;
   const uint32_t kv_off = (uint32_t)(st_row * tok_stride + st_c * 16);
   const uint32_t rp_off = (uint32_t)(st_row * (D / 2) * 8 + st_c * 64);
   u32x4 kraw, vraw;
   f32x4 kcs[4];
-  auto stage_load = [&](int kt0) {
+  auto stage_load_k = [&](int kt0) {
     if (!st_on) return;
     const int rows = N - kt0;
     const uint32_t kv_bytes = rows > 0 ? (uint32_t)((rows - 1) * tok_stride + D) : 0u;
     const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 8) : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, kv_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)kt0 * tok_stride, kv_bytes);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rope + (size_t)kt0 * (D / 2), rp_bytes);
     kraw = buffer_load_b128(rk, kv_off);
-    vraw = buffer_load_b128(rv, kv_off);
 #pragma unroll
     for (int i = 0; i < 4; ++i) kcs[i] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off + 16 * i));
   };
-  auto stage_store = [&](int buf) {
+  auto stage_load_v = [&](int kt0) {
     if (!st_on) return;
-    FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
-    FLUX_LDS char* vl = (FLUX_LDS char*)vsm[buf];
-    lds_write_b128(kl + st_row * C::K8ROW + st_c * 16, rope16_e4m3(kraw, kcs));
-    u32x4 lo, hi;
-    e4m3x16_to_bf16(vraw, &lo, &hi);
-    lds_write_b128(vl + v_off<D>(st_row, 2 * st_c), lo);
-    lds_write_b128(vl + v_off<D>(st_row, 2 * st_c + 1), hi);
+    const int rows = N - kt0;
+    const uint32_t kv_bytes = rows > 0 ? (uint32_t)((rows - 1) * tok_stride + D) : 0u;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)kt0 * tok_stride, kv_bytes);
+    vraw = buffer_load_b128(rv, kv_off);
   };
-
   f32x16 o[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) o[db] = (f32x16){};
-  float m_ref = -INFINITY;  // running max of the scaled score, exp2 domain
+  float m_ref = 0.f;  // reference of the scaled score (exp2 domain): p = exp2(s * sc - m_ref)
   float lsum = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int grp = lane >> 4, li = lane & 15;
 
+  auto kfrag = [&](const FLUX_LDS char* kl, int kb, int t) -> i32x8 {
+    const FLUX_LDS char* p = kl + (32 * kb + krow_perm(l32)) * C::K8ROW + 64 * t + 32 * g;
+    const u32x4 x0 = lds_read_b128(p), x1 = lds_read_b128(p + 16);
+    const uint32_t w[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    return __builtin_bit_cast(i32x8, w);
+  };
   auto qk = [&](const FLUX_LDS char* kl, int kb) -> f32x16 {
-    const int krow = 32 * kb + krow_perm(l32);
     i32x8 kf[C::KS8];
 #pragma unroll
-    for (int t = 0; t < C::KS8; ++t) {
-      const FLUX_LDS char* p = kl + krow * C::K8ROW + 64 * t + 32 * g;
-      const u32x4 x0 = lds_read_b128(p), x1 = lds_read_b128(p + 16);
-      const uint32_t w[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      kf[t] = __builtin_bit_cast(i32x8, w);
-    }
+    for (int t = 0; t < C::KS8; ++t) kf[t] = kfrag(kl, kb, t);
     f32x16 s = {};
 #pragma unroll
     for (int t = 0; t < C::KS8; ++t) s = mfma_fp8(kf[t], qf[t], s);
@@ -205,40 +208,34 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
       if (key >= N) s[e] = -INFINITY;
     }
   };
-  // Lazy running max in the exp2 domain: moves only when a row's block max
-  // exceeds it by more than 8 (p stays <= 256).
-  auto update_max = [&](const f32x16& s, float* alpha) -> bool {
+  // Reference m as in the bf16 kernel: the first tile of the range sets it to
+  // the row max; later tiles form p directly and only move it when a row's
+  // tile sum reaches 2^32 (or is not finite).
+  auto block_max = [&](const f32x16& s) -> float {
     float mt = s[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
-    mt = fmaxf(mt, swap_halves(mt));
-    const float ms = mt * sc;
-    const bool need = ms > m_ref + 8.0f;
-    *alpha = 1.0f;
-    if (__ballot(need) == 0) return false;
-    *alpha = need ? __builtin_amdgcn_exp2f(m_ref - ms) : 1.0f;
-    m_ref = need ? ms : m_ref;
-    return true;
+    return fmaxf(mt, swap_halves(mt)) * sc;
   };
   auto rescale_o = [&](float alpha) {
     lsum *= alpha;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
   };
-  auto make_p = [&](const f32x16& s, int hh) -> u32x4 {
+  auto p_pair = [&](float x0, float x1, float& bsum) -> uint32_t {
+    bf16x2 q2;
+    q2[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(x0, sc, -m_ref));
+    q2[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(x1, sc, -m_ref));
+    bsum = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, bsum, false);
+    return __builtin_bit_cast(uint32_t, q2);
+  };
+  auto make_p = [&](const f32x16& s, int hh, float& bsum) -> u32x4 {
     u32x4 pf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hh + 2 * i], sc, -m_ref));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hh + 2 * i + 1], sc, -m_ref));
-      bf16x2 pp;
-      pp[0] = (__bf16)p0;
-      pp[1] = (__bf16)p1;
-      pf[i] = __builtin_bit_cast(uint32_t, pp);
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-    }
+    for (int i = 0; i < 4; ++i) pf[i] = p_pair(s[8 * hh + 2 * i], s[8 * hh + 2 * i + 1], bsum);
     return pf;
   };
+  auto block_ok = [&](float bsum) -> bool { return __ballot(!(bsum < 0x1p32f)) == 0; };
   auto pv = [&](const FLUX_LDS char* vl, int kb, int hh, const u32x4& pf) {
     const int krow0 = 32 * kb + 16 * hh + 8 * (grp >> 1) + (li >> 2);
 #pragma unroll
@@ -251,60 +248,174 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
       o[db] = mfma_bf16(__builtin_bit_cast(bf16x8, vv), __builtin_bit_cast(bf16x8, pf), o[db]);
     }
   };
+  auto store_k = [&](int buf) {
+    if (!st_on) return;
+    FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
+    lds_write_b128(kl + st_row * C::K8ROW + st_c * 16, rope16_e4m3(kraw, kcs));
+  };
+  auto store_v = [&](int buf) {
+    if (!st_on) return;
+    FLUX_LDS char* vl = (FLUX_LDS char*)vsm[buf];
+    u32x4 lo, hi;
+    e4m3x16_to_bf16(vraw, &lo, &hi);
+    lds_write_b128(vl + v_off<D>(st_row, 2 * st_c), lo);
+    lds_write_b128(vl + v_off<D>(st_row, 2 * st_c + 1), hi);
+  };
 
-  stage_load(kv0 * C::BN);
-  stage_store(0);
-  stage_load((kv0 + 1) * C::BN);
+  // Software pipeline over 64-key tiles, as in the bf16 kernel.  Iteration t:
+  //   MFMA:  S(t) = QK(t) (fp8), then O += PV(t-1) (bf16) with P(t-1);
+  //   VALU:  RoPE + requantization and LDS store of K(t+1), widening and store
+  //          of V(t) beside them; P(t) beside PV; global loads of the next tiles.
+  //   barrier.
+  // K(t+1) and V(t) go into the buffers that K(t-1) and V(t-2) held.
+  stage_load_k(kv0 * C::BN);
+  store_k(0);
+  stage_load_k((kv0 + 1) * C::BN);
+  stage_load_v(kv0 * C::BN);
   __syncthreads();
 
-  // Per tile: S0 = QK(block 0) || store of tile j+1; S1 = QK(block 1) || P of
-  // block 0 and loads of tile j+2; O += PV(block 0) || P of block 1;
-  // O += PV(block 1).  Same buffer discipline as the bf16 kernel.
-  auto tile_step = [&](int j, auto last_tag) {
+  u32x4 pp[4];  // P(t-1): fragments (block 0, keys 0-15), (0, 16-31), (1, 0-15), (1, 16-31)
+  auto rare_move = [&](f32x16& s0, f32x16& s1, float& b) {
+    const float m_new = fmaxf(m_ref, bf16_round(fmaxf(block_max(s0), block_max(s1))));
+    rescale_o(__builtin_amdgcn_exp2f(m_ref - m_new));
+    m_ref = m_new;
+    b = 0.f;
+    pp[0] = make_p(s0, 0, b);
+    pp[1] = make_p(s0, 1, b);
+    pp[2] = make_p(s1, 0, b);
+    pp[3] = make_p(s1, 1, b);
+  };
+  // The first tile of the range (no PV yet): its row max sets m.
+  auto step_first = [&](auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
-    const int buf = (j - kv0) & 1;
-    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[buf];
-    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[buf];
-    const int kt0 = j * C::BN;
-    float alpha;
-
+    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[0];
+    const int kt0 = kv0 * C::BN;
     f32x16 s0 = qk(kl, 0);
-    stage_store(buf ^ 1);
-    if (LAST) mask(kt0, 0, s0);
-    if (update_max(s0, &alpha)) rescale_o(alpha);
-
     f32x16 s1 = qk(kl, 1);
-    const u32x4 p00 = make_p(s0, 0);
-    const u32x4 p01 = make_p(s0, 1);
-    stage_load((j + 2) * C::BN);
-    sched_interleave<C::KS8, 8>();
-    if (LAST) mask(kt0, 1, s1);
-    if (update_max(s1, &alpha)) {
-      rescale_o(alpha);
-      // P of block 0 was formed with the old reference: rescale it too.
-      u32x4 q0 = p00, q1 = p01;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        q0[i] = pack_bf16(bf16lo(q0[i]) * alpha, bf16hi(q0[i]) * alpha);
-        q1[i] = pack_bf16(bf16lo(q1[i]) * alpha, bf16hi(q1[i]) * alpha);
-      }
-      pv(vl, 0, 0, q0);
-      pv(vl, 0, 1, q1);
-    } else {
-      pv(vl, 0, 0, p00);
-      pv(vl, 0, 1, p01);
+    if (LAST) {
+      mask(kt0, 0, s0);
+      mask(kt0, 1, s1);
     }
-    const u32x4 p10 = make_p(s1, 0);
-    const u32x4 p11 = make_p(s1, 1);
-    pv(vl, 1, 0, p10);
-    pv(vl, 1, 1, p11);
-    sched_interleave<2 * C::DB, 4>();
+    m_ref = bf16_round(fmaxf(block_max(s0), block_max(s1)));
+    float b = 0.f;
+    pp[0] = make_p(s0, 0, b);
+    pp[1] = make_p(s0, 1, b);
+    pp[2] = make_p(s1, 0, b);
+    pp[3] = make_p(s1, 1, b);
+    if (!block_ok(b)) rare_move(s0, s1, b);
+    lsum += b;
+    store_k(1);
+    store_v(0);
+    stage_load_k((kv0 + 2) * C::BN);
+    stage_load_v((kv0 + 1) * C::BN);
+    __syncthreads();
+  };
+  // Every later tile: one fixed-order MFMA stream (QK(t), then PV(t-1)), each
+  // MFMA followed by its operand reads NPF MFMAs ahead and a slice of VALU work.
+  auto step_main = [&](int t, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const int i = t - kv0;
+    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[i & 1];
+    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[(i + 1) & 1];  // V(t-1)
+    const int kt0 = t * C::BN;
+    constexpr int NK = 2 * C::KS8, NV = 4 * C::DB, NL = NK + NV;
+    auto vfrag = [&](int v) -> u32x4 {
+      const int kb = v / (2 * C::DB), hh = (v / C::DB) & 1, db = v % C::DB;
+      const int krow0 = 32 * kb + 16 * hh + 8 * (grp >> 1) + (li >> 2);
+      const int d = 32 * db + 16 * (grp & 1) + 4 * (li & 3);
+      const u32x2 lo = lds_read_tr16(vl + v_off<D>(krow0, d >> 3) + (d & 7) * 2);
+      const u32x2 hi = lds_read_tr16(vl + v_off<D>(krow0 + 4, d >> 3) + (d & 7) * 2);
+      return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+    };
+    // K fragments are read two MFMAs ahead, V fragments NPF ahead.
+    constexpr int NPF = 3;
+    i32x8 fk[2];
+    u32x4 fv[NPF];
+    fk[0] = kfrag(kl, 0, 0);
+    if constexpr (NK > 1) fk[1] = kfrag(kl, 1 / C::KS8, 1 % C::KS8);
+    FLUX_LDS char* kw = (FLUX_LDS char*)ksm[(i + 1) & 1];  // K(t+1)
+    FLUX_LDS char* vw = (FLUX_LDS char*)vsm[i & 1];        // V(t)
+    u32x4 ky, vlo, vhi;
+    f32x16 s0 = (f32x16){}, s1 = (f32x16){};
+    float b = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NL>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < NK) {
+        const i32x8 x = fk[j % 2];
+        if constexpr (j + 2 < NK) fk[j % 2] = kfrag(kl, (j + 2) / C::KS8, (j + 2) % C::KS8);
+        if constexpr (j < C::KS8) s0 = mfma_fp8(x, qf[j], s0);
+        else s1 = mfma_fp8(x, qf[j - C::KS8], s1);
+      } else {
+        constexpr int v = j - NK, q4 = v / C::DB, db = v % C::DB;
+        const u32x4 x = fv[v % NPF];
+        o[db] = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, pp[q4]), o[db]);
+      }
+      // V fragment v is read in slot NK + v - NPF (or before the first PV MFMA)
+      constexpr int vn = j - NK + NPF;
+      if constexpr (j >= NK - 1 && j < NK) {
+#pragma unroll
+        for (int v0 = 0; v0 < NPF; ++v0) fv[v0] = vfrag(v0);
+      } else if constexpr (j >= NK && vn < NV) {
+        fv[vn % NPF] = vfrag(vn);
+      }
+      // staging: RoPE of K(t+1) one dword per slot, then its store; V(t)
+      // widened and stored; loads of K(t+2) and V(t+1)
+      constexpr int R0 = NK;  // first staging slot
+      if constexpr (j >= R0 && j < R0 + 4) {
+        if (st_on) ky[j - R0] = rope_dword_e4m3(kraw[j - R0], kcs[j - R0]);
+        if constexpr (j == R0 + 3) {
+          if (st_on) lds_write_b128(kw + st_row * C::K8ROW + st_c * 16, ky);
+        }
+      }
+      if constexpr (j == R0 + 4) {
+        if (st_on) {
+          e4m3x16_to_bf16(vraw, &vlo, &vhi);
+          lds_write_b128(vw + v_off<D>(st_row, 2 * st_c), vlo);
+          lds_write_b128(vw + v_off<D>(st_row, 2 * st_c + 1), vhi);
+        }
+      }
+      if constexpr (j == R0 + 5) stage_load_k((t + 2) * C::BN);
+      if constexpr (j == R0 + 6) stage_load_v((t + 1) * C::BN);
+      if constexpr (j >= NK) {
+        constexpr int v = j - NK;
+        if (LAST && v == 0) mask(kt0, 0, s0);
+        if (LAST && v == 1) mask(kt0, 1, s1);
+        if constexpr (v >= C::DB) {  // P(t) slice q replaces P(t-1) slice q
+          constexpr int q = (v - C::DB) / C::DB, e = (v - C::DB) % C::DB;
+          const f32x16& sq = q < 2 ? s0 : s1;
+          constexpr int hh = q & 1;
+#pragma unroll
+          for (int ee = 0; ee < 4 / C::DB; ++ee) {
+            const int e2 = e * (4 / C::DB) + ee;
+            pp[q][e2] = p_pair(sq[8 * hh + 2 * e2], sq[8 * hh + 2 * e2 + 1], b);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) pp[3][e2] = p_pair(s1[8 + 2 * e2], s1[8 + 2 * e2 + 1], b);
+    if (!block_ok(b)) rare_move(s0, s1, b);  // rare
+    lsum += b;
     __syncthreads();
   };
 
-  const int full_end = min(kv1, N / C::BN);
-  for (int j = kv0; j < full_end; ++j) tile_step(j, std::false_type{});
-  if (full_end < kv1) tile_step(full_end, std::true_type{});
+  const int full_end = min(kv1, N / C::BN);  // tiles before this one are full
+  if (kv0 < full_end) {
+    step_first(std::false_type{});
+    for (int t = kv0 + 1; t < full_end; ++t) step_main(t, std::false_type{});
+    if (full_end < kv1) step_main(full_end, std::true_type{});
+  } else {
+    step_first(std::true_type{});
+  }
+  {
+    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[(kv1 - 1 - kv0) & 1];
+    pv(vl, 0, 0, pp[0]);
+    pv(vl, 0, 1, pp[1]);
+    pv(vl, 1, 0, pp[2]);
+    pv(vl, 1, 1, pp[3]);
+  }
 
   const float ltot = lsum + swap_halves(lsum);
   if (slot >= 0) {
