@@ -11,7 +11,9 @@ What it computes (every function cites the passage it follows):
   * ``softmax_attention`` - non-causal softmax attention over the whole joint sequence,
                      blocked over query rows, fp64;
   * ``e4m3``       - decoding of OCP 8-bit e4m3 ("e4m3fn") codes from the
-                     format's definition.
+                     format's definition;
+  * ``block_sparse`` - the tile-mask rule of threshold-sparse attention and
+                     exact attention over the kept tiles.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle.py`` (closed forms, brute force, independent formulations,
@@ -25,3 +27,4 @@ from .softmax_attention import (softmax_rows, attention_from_scores, attention, 
                         segment_local_rope_attention)
 from .e4m3 import e4m3_decode, e4m3_table, dequantize  # noqa: F401
 from .inputs_fp64 import inputs_to_fp64  # noqa: F401
+from .block_sparse import tile_means, block_scores, block_mask, block_sparse_attention  # noqa: F401

@@ -1,0 +1,155 @@
+"""Pins of the tile-sparse oracle (oracle/block_sparse.py) against facts that do
+not come from it: a hand-worked mask, the extremes of tau, bilinearity of the
+pooled score (the mean of the per-pair scores of the full score matrix), an
+all-kept mask reducing to the dense oracle, brute-force loops on tiny inputs
+and torch's scaled_dot_product_attention with the equivalent boolean mask.
+A mutation check plants plausible mistakes in copies of the functions.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import block_sparse as obs
+
+AXES = (8, 12, 12)  # D = 32
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _pos(n, seed=0):
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 40, size=(n, 3)).astype(np.int32)
+
+
+def test_hand_worked_mask():
+    # D = 2, RoPE off (positions 0), scale 1: q tiles of 2 tokens, k tiles of 1.
+    # q tile 0 = rows (1, 0), (3, 0): mean (2, 0); q tile 1 = (0, 1), (0, 3): mean (0, 2).
+    # keys (1, 0), (0, 1), (1, 1): pooled dots: tile 0 -> 2, 0, 2; tile 1 -> 0, 2, 2.
+    q = np.array([[1, 0], [3, 0], [0, 1], [0, 3]], float).reshape(1, 4, 1, 2)
+    k = np.array([[1, 0], [0, 1], [1, 1]], float).reshape(1, 3, 1, 2)
+    pos = np.zeros((4, 3), np.int32)
+    s = obs.block_scores(q, np.concatenate([k, np.zeros((1, 1, 1, 2))], axis=1), pos, (0, 0, 2),
+                         q_tile=2, k_tile=1, scale=1.0)
+    l2e = 1.0 / math.log(2.0)
+    np.testing.assert_allclose(s[0, 0], l2e * np.array([[2, 0, 2, 0], [0, 2, 2, 0]]), rtol=1e-15)
+    mask, margin = obs.block_mask(s, tau=0.25)   # keep score >= max - 2 (exp2 domain)
+    # max = 2 * l2e = 2.885; threshold 0.885: keys with pooled dot 2 kept, 0 dropped
+    assert mask[0, 0].tolist() == [[True, False, True, False], [False, True, True, False]]
+    np.testing.assert_allclose(margin[0, 0, 0, 0], 2.0, rtol=1e-14)
+
+
+def test_tau_extremes():
+    q, k = _rand((2, 50, 3, 32), 1), _rand((2, 50, 3, 32), 2)
+    pos = _pos(50)
+    s = obs.block_scores(q, k, pos, AXES, q_tile=16, k_tile=8)
+    m1, _ = obs.block_mask(s, 1.0)
+    assert (m1 == (s == s.max(axis=-1, keepdims=True))).all()
+    assert m1.sum(axis=-1).min() >= 1
+    m0, _ = obs.block_mask(s, 1e-300)
+    assert m0.all()
+    with pytest.raises(ValueError):
+        obs.block_mask(s, 0.0)
+
+
+def test_pooled_score_is_mean_of_pair_scores():
+    # Bilinearity: <mean q, mean k> is the mean over the tile pair of <q_i, k_j>.
+    B, N, H, D = 1, 37, 2, 32
+    q, k = _rand((B, N, H, D), 3), _rand((B, N, H, D), 4)
+    pos = _pos(N, 1)
+    qr, kr = oracle.apply_rope(q, pos, AXES), oracle.apply_rope(k, pos, AXES)
+    full = np.einsum("bihd,bjhd->bhij", qr, kr) / math.sqrt(D) / math.log(2.0)
+    s = obs.block_scores(q, k, pos, AXES, q_tile=10, k_tile=6)
+    for qt in range(4):
+        for kt in range(7):
+            blk = full[:, :, qt * 10:(qt + 1) * 10, kt * 6:(kt + 1) * 6]
+            np.testing.assert_allclose(s[:, :, qt, kt], blk.mean(axis=(-1, -2)), rtol=1e-12, atol=1e-12)
+
+
+def test_all_kept_equals_dense_oracle():
+    B, N, H, D = 1, 45, 2, 32
+    q, k, v = _rand((B, N, H, D), 5), _rand((B, N, H, D), 6), _rand((B, N, H, D), 7)
+    pos = _pos(N, 2)
+    mask = np.ones((B, H, 3, 6), bool)
+    got = obs.block_sparse_attention(q, k, v, pos, AXES, mask, q_tile=16, k_tile=8)
+    np.testing.assert_allclose(got, oracle.joint_rope_attention(q, k, v, pos, AXES), rtol=1e-12, atol=1e-13)
+
+
+def _brute(q, k, v, pos, mask, qt_sz, kt_sz):
+    """Triple loops: masked scores set aside, softmax written out."""
+    qr, kr = oracle.apply_rope(q, pos, AXES), oracle.apply_rope(k, pos, AXES)
+    B, N, H, D = q.shape
+    out = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                w = []
+                for j in range(N):
+                    if mask[b, h, i // qt_sz, j // kt_sz]:
+                        w.append((sum(qr[b, i, h, d] * kr[b, j, h, d] for d in range(D)) / math.sqrt(D), j))
+                if not w:
+                    continue
+                mx = max(x for x, _ in w)
+                z = sum(math.exp(x - mx) for x, _ in w)
+                for x, j in w:
+                    out[b, i, h] += math.exp(x - mx) / z * v[b, j, h]
+    return out
+
+
+def test_brute_force_tiny():
+    B, N, H, D = 1, 11, 2, 32
+    q, k, v = _rand((B, N, H, D), 8), _rand((B, N, H, D), 9), _rand((B, N, H, D), 10)
+    pos = _pos(N, 3)
+    rng = np.random.default_rng(11)
+    mask = rng.random((B, H, 3, 4)) < 0.5
+    mask[0, 0, 2] = False          # a query tile with nothing kept -> zeros
+    mask[0, 1, :, 0] = True
+    got = obs.block_sparse_attention(q, k, v, pos, AXES, mask, q_tile=4, k_tile=3)
+    np.testing.assert_allclose(got, _brute(q, k, v, pos, mask, 4, 3), rtol=1e-11, atol=1e-12)
+    assert np.all(got[0, 8:, 0] == 0.0)
+
+
+def test_torch_sdpa_with_boolean_mask():
+    torch = pytest.importorskip("torch")
+    B, N, H, D = 1, 70, 2, 32
+    q, k, v = _rand((B, N, H, D), 12), _rand((B, N, H, D), 13), _rand((B, N, H, D), 14)
+    pos = _pos(N, 4)
+    rng = np.random.default_rng(15)
+    mask = rng.random((B, H, 3, 9)) < 0.4
+    mask[..., 0] = True
+    got = obs.block_sparse_attention(q, k, v, pos, AXES, mask, q_tile=32, k_tile=8)
+    qr, kr = oracle.apply_rope(q, pos, AXES), oracle.apply_rope(k, pos, AXES)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+    tok_mask = np.repeat(np.repeat(mask, 32, axis=2)[:, :, :N], 8, axis=3)[:, :, :, :N]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(qr), t(kr), t(v), attn_mask=torch.from_numpy(tok_mask))
+    np.testing.assert_allclose(got, ref.numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-12)
+
+
+def test_mutations_are_caught():
+    B, N, H, D = 1, 11, 2, 32
+    q, k, v = _rand((B, N, H, D), 16), _rand((B, N, H, D), 17), _rand((B, N, H, D), 18)
+    pos = _pos(N, 5)
+    mask = np.random.default_rng(19).random((B, H, 3, 4)) < 0.6
+    mask[..., 0] = True
+    ref = _brute(q, k, v, pos, mask, 4, 3)
+    orig = obs.block_sparse_attention
+
+    def off_by_one_tile(q, k, v, pos, axes, m, q_tile, k_tile, **kw):
+        return orig(q, k, v, pos, axes, np.roll(m, 1, axis=-1), q_tile, k_tile, **kw)
+
+    def transposed_mask(q, k, v, pos, axes, m, q_tile, k_tile, **kw):
+        m2 = np.zeros_like(m)
+        n = min(m.shape[-1], m.shape[-2])
+        m2[..., :n, :n] = np.swapaxes(m[..., :n, :n], -1, -2)
+        return orig(q, k, v, pos, axes, m2 | (np.arange(m.shape[-1]) == 0), q_tile, k_tile, **kw)
+
+    for bad in (off_by_one_tile, transposed_mask):
+        got = bad(q, k, v, pos, AXES, mask, 4, 3)
+        assert not np.allclose(got, ref, rtol=1e-6, atol=1e-8), bad.__name__
+    s = obs.block_scores(q, k, pos, AXES, q_tile=4, k_tile=3)
+    m_good, _ = obs.block_mask(s, 0.3)
+    m_wrong_sign = s <= s.max(axis=-1, keepdims=True) + math.log2(0.3)
+    assert (m_good != m_wrong_sign).any()
