@@ -11,8 +11,10 @@ tokens (8,704), 24 heads, head_dim 128, bf16 Q/K/V ~ N(0, 0.25).  Inputs are
 resident in HBM before timing starts.  The 4,608-token text-to-image call, the
 66,048-token e4m3 call, the edit call in segment-local mode (each segment
 attending to itself), one GPU's share of the edit call under 8-way head
-sharding (3 heads, split K/V schedule) and, with --all, the 25,088-token call
-are reported as extra fields of the same JSON line.
+sharding (3 heads, split K/V schedule), tile-sparse attention on edit-call
+tokens with position-local attention (thresholds 0.1 and 0.01) and, with
+--all, the 25,088-token call are reported as extra fields of the same JSON
+line.
 
 Rank 0 prints one JSON line.  Only one GPU is supported: the path shards over
 heads with no communication inside the kernel, and this build measures one
@@ -122,6 +124,62 @@ def measure(workload, steps, warmup, mode="joint"):
     }
 
 
+def measure_sparse(workload, tau, steps, warmup):
+    """Tile-sparse attention: the tile mask of threshold tau (built and timed
+    once), then forward_sparse timed like forward."""
+    import numpy as np
+    import torch
+    from diffusion_transformer_joint_amd import inputs as I
+    from diffusion_transformer_joint_amd.flux_attn import Plan
+
+    w = I.WORKLOADS[workload]
+    inp = I.make_inputs(w)
+    dev = torch.device("cuda:0")
+    cv = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+    q, k, v = cv(inp.q), cv(inp.k), cv(inp.v)
+    pos = torch.from_numpy(inp.pos).to(dev)
+    out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    plan = Plan(w.batch, w.heads, w.head_dim, w.tokens)
+    segs = w.segment_tokens
+    mask = plan.block_mask(q, k, segs, pos, tau)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        plan.block_mask(q, k, segs, pos, tau, mask=mask)
+    e1.record()
+    torch.cuda.synchronize()
+    mask_ms = e0.elapsed_time(e1) / steps
+    for _ in range(warmup):
+        plan.forward_sparse(q, k, v, segs, pos, mask, out=out)
+    torch.cuda.synchronize()
+    plan.timing_enable(steps)
+    e0.record()
+    for _ in range(steps):
+        plan.forward_sparse(q, k, v, segs, pos, mask, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    kernel_ms = plan.timing_read()
+    plan.close()
+    step_ms = e0.elapsed_time(e1) / steps
+    m = mask.cpu().numpy().astype(bool)
+    n = w.tokens
+    rows_per_qt = np.minimum(256, n - 256 * np.arange(m.shape[2]))
+    keys_per_kt = np.minimum(64, n - 64 * np.arange(m.shape[3]))
+    kept_pairs = float(np.einsum("bhqk,q,k->", m.astype(np.float64), rows_per_qt, keys_per_kt))
+    kavg = sum(kernel_ms) / len(kernel_ms)
+    dense_flops = w.flops()
+    kept_flops = 4.0 * w.head_dim * kept_pairs
+    return {
+        "workload": f"{w.name} (tile-sparse, tau {tau})", "tokens": n, "heads": w.heads, "head_dim": w.head_dim,
+        "batch": w.batch, "dtype": "bf16", "tau": tau, "kept_tile_fraction": float(m.mean()),
+        "kept_pair_fraction": kept_pairs / (w.batch * w.heads * n * n),
+        "mask_ms": mask_ms, "ms_per_step": step_ms, "kernel_ms_avg": kavg,
+        "flops": kept_flops, "kernel_tflops": kept_flops / (kavg * 1e-3) / 1e12,
+        "dense_equivalent_tflops": dense_flops / (kavg * 1e-3) / 1e12,
+    }
+
+
 def cpu_baseline(workload, rows_count):
     """The fp64 oracle, as it stands, on a bounded sample of query rows."""
     import numpy as np
@@ -205,6 +263,12 @@ def main():
             r["frac_mixed_ceiling"] = r["kernel_tflops"] / (2.0 / (1.0 / FP8_PEAK + 1.0 / BF16_PEAK))
         extra.append(r)
         log(f"{r['workload']}: {r['kernel_tflops']:.1f} TFLOP/s kernel")
+    for tau in (0.1, 0.01):
+        r = measure_sparse("edit1024_local", tau, max(5, args.steps // 2), max(2, args.warmup // 2))
+        r["speedup_vs_dense_edit1024"] = main_run["kernel_ms_avg"] / r["kernel_ms_avg"]
+        extra.append(r)
+        log(f"{r['workload']}: kept {r['kept_pair_fraction']:.2f} of pairs, {r['kernel_ms_avg']:.3f} ms, "
+            f"{r['kernel_tflops']:.1f} TFLOP/s on kept pairs, x{r['speedup_vs_dense_edit1024']:.2f} vs dense")
 
     kernel = "attn_bf16"
     traffic = recorded_traffic(kernel, args.workload)

@@ -51,7 +51,7 @@ struct Bf16Cfg {
   static constexpr int VTILEB = BN * (2 * D + 64);  // bytes per V tile in LDS
 };
 
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_kernel(AttnArgs a) {
   using C = Bf16Cfg<D>;
@@ -60,16 +60,29 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
 
   const int N = a.n_tokens, H = a.heads;
   const int n_tiles = (N + C::BN - 1) / C::BN;
-  int tile, kv0 = 0, kv1 = n_tiles, slot = -1;
+  int tile, slot = -1, piece = 0;
   if ((int)blockIdx.x < a.whole) {
     tile = xcd_tile_order(blockIdx.x, a.whole);
   } else {
     slot = blockIdx.x - a.whole;
     tile = a.whole + slot / a.split;
-    const int piece = slot % a.split;
-    kv0 = piece * n_tiles / a.split;
-    kv1 = (piece + 1) * n_tiles / a.split;
+    piece = slot % a.split;
   }
+  // The 64-key tiles this query tile attends to, by position p: all of them
+  // (p itself), or in a tile-sparse launch the kept list.  A split piece runs
+  // positions [kv0, kv1).  Positions past the range map to a tile past N,
+  // whose loads read zeros.
+  const int* kvlist = SPARSE ? a.kv_list + (size_t)tile * a.list_stride : nullptr;
+  const int cnt = SPARSE ? a.kv_count[tile] : n_tiles;
+  int kv0 = 0, kv1 = cnt;
+  if (slot >= 0) {
+    kv0 = piece * cnt / a.split;
+    kv1 = (piece + 1) * cnt / a.split;
+  }
+  auto kvt = [&](int p) -> int {
+    if constexpr (SPARSE) return p < kv1 ? kvlist[p] : n_tiles;
+    else return p;
+  };
   const int qt = tile % a.q_tiles;
   const int bh = tile / a.q_tiles;
   const int h = bh % H, b = bh / H;
@@ -258,10 +271,11 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   //   barrier.
   // K(t) is read in iteration t and V(t) in iteration t+1, so K(t+1) and V(t)
   // are written into the buffers that K(t-1) and V(t-2) held: two buffers each.
-  load_k(kv0 * C::BN);
+  if (kv0 < kv1) {  // (a tile-sparse range may be empty: O = 0)
+  load_k(kvt(kv0) * C::BN);
   store_k(0);
-  load_k((kv0 + 1) * C::BN);
-  load_v(kv0 * C::BN);
+  load_k(kvt(kv0 + 1) * C::BN);
+  load_v(kvt(kv0) * C::BN);
   __syncthreads();
 
   u32x4 pp[4];  // P(t-1): fragments (block 0, keys 0-15), (0, 16-31), (1, 0-15), (1, 16-31)
@@ -269,7 +283,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   auto step_first = [&](auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
     const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[0];
-    const int kt0 = kv0 * C::BN;
+    const int kt0 = kvt(kv0) * C::BN;
 
     f32x16 s0 = qk(kl, 0);
     f32x16 s1 = qk(kl, 1);
@@ -303,8 +317,8 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     lsum += b;
     store_k(1);
     store_v(0);
-    load_k((kv0 + 2) * C::BN);
-    load_v((kv0 + 1) * C::BN);
+    load_k(kvt(kv0 + 2) * C::BN);
+    load_v(kvt(kv0 + 1) * C::BN);
     __syncthreads();
   };
 
@@ -331,7 +345,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[(i + 1) & 1];  // V(t-1)
     FLUX_LDS char* kw = (FLUX_LDS char*)ksm[(i + 1) & 1];              // K(t+1)
     FLUX_LDS char* vw = (FLUX_LDS char*)vsm[i & 1];                    // V(t)
-    const int kt0 = t * C::BN;
+    const int kt0 = kvt(t) * C::BN;
     // MFMA j < NK: S(t), K fragment j; NK <= j < NL: PV(t-1), V fragment j - NK.
     constexpr int NK = 2 * C::KSTEPS, NL = NK + 4 * C::DB;
     auto ld = [&](int j) -> u32x4 {
@@ -384,8 +398,8 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
         constexpr int p = j == VST0 ? 0 : 1;
         lds_write_b128(vw + v_off<D>(st_row0 + p * C::RPP, st_chunk), vraw[p]);
       }
-      if constexpr (j == LVS) load_v((t + 1) * C::BN);
-      if constexpr (j == LKS) load_k((t + 2) * C::BN);
+      if constexpr (j == LVS) load_v(kvt(t + 1) * C::BN);
+      if constexpr (j == LKS) load_k(kvt(t + 2) * C::BN);
       if constexpr (j >= NK) {
         constexpr int v = j - NK;
         if (LAST && v == 0) mask(kt0, 0, s0);
@@ -421,7 +435,8 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     __syncthreads();
   };
 
-  const int full_end = min(kv1, N / C::BN);  // tiles before this one are full
+  // positions before full_end hold full tiles; the last one may be ragged
+  const int full_end = (N % C::BN != 0 && kvt(kv1 - 1) == n_tiles - 1) ? kv1 - 1 : kv1;
   if (kv0 < full_end) {
     step_first(std::false_type{});
     for (int t = kv0 + 1; t < full_end; ++t) step_main(t, std::false_type{});
@@ -436,6 +451,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     pv(vl, 1, 0, pp[2]);
     pv(vl, 1, 1, pp[3]);
   }
+  }  // kv0 < kv1
 
   // ---- epilogue.  A K/V range of a split tile stores its fp32 partial state.
   const float ltot = lsum + swap_halves(lsum);
@@ -449,11 +465,11 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
         const f32x4 w = {o[db][4 * aa], o[db][4 * aa + 1], o[db][4 * aa + 2], o[db][4 * aa + 3]};
         *(f32x4*)(po + 32 * db + 8 * aa + 4 * g) = w;
       }
-    if (g == 0) a.part_ml[(size_t)slot * C::BM + r] = make_float2(m_ref, ltot);
+    if (g == 0) a.part_ml[(size_t)slot * C::BM + r] = make_float2(kv0 < kv1 ? m_ref : -INFINITY, ltot);
     return;
   }
   // ---- epilogue: O = O^T / l, bf16, stored row-major.
-  const float inv = 1.0f / ltot;
+  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // 0: an empty tile-sparse range
   if (qrow < N) {
     uint16_t* orow = a.o + bat + (size_t)qrow * tok_stride + (size_t)h * D;
 #pragma unroll
@@ -489,14 +505,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   float l = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int i = 0; i < a.split; ++i) {
     const float2 ml = a.part_ml[(size_t)(slot0 + i) * 256 + r];
-    const float w = __builtin_amdgcn_exp2f(ml.x - m);
+    const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - m) : 0.f;  // empty ranges weigh 0
     l += w * ml.y;
     const float* po = a.part_o + ((size_t)(slot0 + i) * 256 + r) * D + d0;
     const f32x4 x0 = *(const f32x4*)po, x1 = *(const f32x4*)(po + 4);
     acc[0] += w * x0[0]; acc[1] += w * x0[1]; acc[2] += w * x0[2]; acc[3] += w * x0[3];
     acc[4] += w * x1[0]; acc[5] += w * x1[1]; acc[6] += w * x1[2]; acc[7] += w * x1[3];
   }
-  const float inv = 1.0f / l;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;  // 0: no kept keys (tile-sparse)
   u32x4 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
@@ -509,10 +525,15 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch
   args.q_tiles = (a.n_tokens + 255) / 256;
   args.whole = sch.whole_tiles;
   args.split = sch.split;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3(sch.grid), dim3(Bf16Cfg<128>::NT), 0, stream, args);
+  const bool sparse = a.kv_list != nullptr;
+  if (head_dim == 128 && !sparse)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), dim3(sch.grid), dim3(Bf16Cfg<128>::NT), 0, stream, args);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), dim3(sch.grid), dim3(Bf16Cfg<128>::NT), 0, stream, args);
+  else if (head_dim == 64 && !sparse)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), dim3(sch.grid), dim3(Bf16Cfg<64>::NT), 0, stream, args);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3(sch.grid), dim3(Bf16Cfg<64>::NT), 0, stream, args);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), dim3(sch.grid), dim3(Bf16Cfg<64>::NT), 0, stream, args);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -62,6 +62,11 @@ struct flux_attn_plan {
   double* freq = nullptr;        // [head_dim/2]
   float* part_o = nullptr;       // split-K/V partials: [max_pieces][256][head_dim]
   float2* part_ml = nullptr;     // [max_pieces][256]
+  // tile-sparse workspace (bf16 plans): tile means, kept-tile lists
+  float* qbar = nullptr;         // [B][H][QT][D]
+  float* kbar = nullptr;         // [B][H][KT][D]
+  int* kv_list = nullptr;        // [B*H*QT][KT]
+  int* kv_count = nullptr;       // [B*H*QT]
   int num_cus = 0;
   int max_pieces = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;  // kernel timing pairs
@@ -159,9 +164,12 @@ int flux_attn_validate_config(const flux_attn_config* c) {
   return ok();
 }
 
-int flux_attn_validate_forward(const flux_attn_config* c, const void* q, const void* k, const void* v,
-                               const float* qkv_scale, const int32_t* segment_tokens, int32_t num_segments,
-                               const int32_t* pos_ids, const void* out, int32_t mode) {
+namespace {
+
+// The forward() checks of everything but the output tensor.
+int validate_inputs(const flux_attn_config* c, const void* q, const void* k, const void* v,
+                    const float* qkv_scale, const int32_t* segment_tokens, int32_t num_segments,
+                    const int32_t* pos_ids, int32_t mode, long long* n_out) {
   int st = flux_attn_validate_config(c);
   if (st) return st;
   if (mode != FLUX_ATTN_JOINT && mode != FLUX_ATTN_SEGMENT_LOCAL)
@@ -178,14 +186,28 @@ int flux_attn_validate_forward(const flux_attn_config* c, const void* q, const v
   if (n < 1) return fail(FLUX_ATTN_INVALID_ARGUMENT, "total token count is 0");
   if (n > c->max_tokens)
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "total token count %lld exceeds max_tokens %d", n, c->max_tokens);
-  if (!q || !k || !v || !out || !pos_ids) return fail(FLUX_ATTN_INVALID_ARGUMENT, "a tensor pointer is NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+  if (!q || !k || !v || !pos_ids) return fail(FLUX_ATTN_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(pos_ids) & 3u) != 0)
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "pos_ids must be 4-byte aligned");
   const bool fp8 = c->dtype == FLUX_ATTN_FP8_E4M3;
   if (fp8 && !qkv_scale) return fail(FLUX_ATTN_INVALID_ARGUMENT, "FP8 inputs need qkv_scale");
   if (!fp8 && qkv_scale) return fail(FLUX_ATTN_INVALID_ARGUMENT, "qkv_scale is only used with FP8 inputs");
+  *n_out = n;
+  return ok();
+}
+
+}  // namespace
+
+int flux_attn_validate_forward(const flux_attn_config* c, const void* q, const void* k, const void* v,
+                               const float* qkv_scale, const int32_t* segment_tokens, int32_t num_segments,
+                               const int32_t* pos_ids, const void* out, int32_t mode) {
+  long long n = 0;
+  int st = validate_inputs(c, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, mode, &n);
+  if (st) return st;
+  if (!out) return fail(FLUX_ATTN_INVALID_ARGUMENT, "a tensor pointer is NULL");
+  if (!aligned16(out)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
   const size_t in_bytes = (size_t)c->batch * (size_t)n * c->num_heads * c->head_dim * elem_bytes(c->dtype);
   const size_t out_bytes = (size_t)c->batch * (size_t)n * c->num_heads * c->head_dim * 2;
   if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
@@ -236,11 +258,23 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     e = hipMalloc(&p->part_o, (size_t)p->max_pieces * 256 * cfg->head_dim * sizeof(float));
   if (e == hipSuccess && p->max_pieces > 0)
     e = hipMalloc(&p->part_ml, (size_t)p->max_pieces * 256 * sizeof(float2));
+  if (e == hipSuccess && cfg->dtype == FLUX_ATTN_BF16) {
+    const size_t rows = (size_t)cfg->batch * cfg->num_heads;
+    const size_t qt = (cfg->max_tokens + 255) / 256, kt = (cfg->max_tokens + 63) / 64;
+    e = hipMalloc(&p->qbar, rows * qt * cfg->head_dim * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(&p->kbar, rows * kt * cfg->head_dim * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(&p->kv_list, rows * qt * kt * sizeof(int));
+    if (e == hipSuccess) e = hipMalloc(&p->kv_count, rows * qt * sizeof(int));
+  }
   if (e != hipSuccess) {
     (void)hipFree(p->rope_table);
     (void)hipFree(p->freq);
     (void)hipFree(p->part_o);
     (void)hipFree(p->part_ml);
+    (void)hipFree(p->qbar);
+    (void)hipFree(p->kbar);
+    (void)hipFree(p->kv_list);
+    (void)hipFree(p->kv_count);
     delete p;
     return hip_fail(e, "plan workspace");
   }
@@ -346,6 +380,114 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
   return ok();
 }
 
+namespace {
+
+// Checks shared by the tile-sparse entry points: a live bf16 plan on the
+// current device and the forward() argument rules (joint mode, no scales).
+int sparse_common(flux_attn_plan* plan, const void* q, const void* k, const void* v,
+                  const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, const void* out,
+                  const void* mask, int* n_out) {
+  if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
+  const flux_attn_config& c = plan->cfg;
+  if (c.dtype != FLUX_ATTN_BF16) return fail(FLUX_ATTN_UNSUPPORTED, "tile-sparse attention needs a bf16 plan");
+  long long nn = 0;
+  int st = out ? flux_attn_validate_forward(&c, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, out,
+                                            FLUX_ATTN_JOINT)
+               : validate_inputs(&c, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, FLUX_ATTN_JOINT, &nn);
+  if (st) return st;
+  if (!mask) return fail(FLUX_ATTN_INVALID_ARGUMENT, "mask is NULL");
+  int n = 0;
+  for (int i = 0; i < num_segments; ++i) n += segment_tokens[i];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan was created on device %d, current device is %d", plan->device, dev);
+  *n_out = n;
+  return ok();
+}
+
+float plan_c(const flux_attn_config& c) {
+  const float scale = c.softmax_scale > 0.0f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
+  return scale * 1.4426950408889634f;
+}
+
+}  // namespace
+
+int flux_attn_block_mask(flux_attn_plan* plan, const void* q, const void* k, const int32_t* segment_tokens,
+                         int32_t num_segments, const int32_t* pos_ids, float tau, uint8_t* mask, void* hip_stream) {
+  int n = 0;
+  // v and out are not used here (k stands in for v in the shared checks).
+  int st = sparse_common(plan, q, k, k, segment_tokens, num_segments, pos_ids, nullptr, mask, &n);
+  if (st) return st;
+  if (!(tau > 0.0f && tau <= 1.0f)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "tau must be in (0, 1]");
+  const flux_attn_config& c = plan->cfg;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = flux::launch_rope_table(pos_ids, plan->freq, plan->rope_table, n, c.head_dim, c.rope_axes_dim[0],
+                                         c.rope_axes_dim[1], stream);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  const int QT = (n + 255) / 256, KT = (n + 63) / 64;
+  e = flux::launch_tile_means(static_cast<const uint16_t*>(q), plan->rope_table, plan->qbar, n, n, c.num_heads,
+                              c.batch, c.head_dim, 256, stream);
+  if (e == hipSuccess)
+    e = flux::launch_tile_means(static_cast<const uint16_t*>(k), plan->rope_table, plan->kbar, n, n, c.num_heads,
+                                c.batch, c.head_dim, 64, stream);
+  if (e == hipSuccess)
+    e = flux::launch_block_select(plan->qbar, plan->kbar, mask, c.batch * c.num_heads * QT, QT, KT, c.head_dim,
+                                  plan_c(c), std::log2(tau), stream);
+  if (e != hipSuccess) return hip_fail(e, "block mask launch");
+  return ok();
+}
+
+int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k, const void* v,
+                             const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids,
+                             const uint8_t* mask, void* out, void* hip_stream) {
+  int n = 0;
+  int st = sparse_common(plan, q, k, v, segment_tokens, num_segments, pos_ids, out, mask, &n);
+  if (st) return st;
+  const flux_attn_config& c = plan->cfg;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = flux::launch_rope_table(pos_ids, plan->freq, plan->rope_table, n, c.head_dim, c.rope_axes_dim[0],
+                                         c.rope_axes_dim[1], stream);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  const int QT = (n + 255) / 256, KT = (n + 63) / 64;
+  const int rows = c.batch * c.num_heads * QT;
+  e = flux::launch_mask_to_list(mask, plan->kv_list, plan->kv_count, rows, KT, KT, stream);
+  if (e != hipSuccess) return hip_fail(e, "mask compaction launch");
+  const flux::Schedule sch = flux::plan_schedule(rows, KT, plan->num_cus, plan->max_pieces, c.head_dim);
+  flux::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(out);
+  a.rope = plan->rope_table;
+  a.n_tokens = n;
+  a.batch_tokens = n;
+  a.heads = c.num_heads;
+  a.batch = c.batch;
+  a.c = plan_c(c);
+  a.part_o = plan->part_o;
+  a.part_ml = plan->part_ml;
+  a.kv_list = plan->kv_list;
+  a.kv_count = plan->kv_count;
+  a.list_stride = KT;
+  const bool timed = plan->timing_used < (int)plan->ev_start.size();
+  if (timed) {
+    e = hipEventRecord(plan->ev_start[plan->timing_used], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  e = flux::launch_attn_bf16(a, c.head_dim, sch, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (timed) {
+    e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    ++plan->timing_used;
+  }
+  e = flux::launch_attn_merge(a, c.head_dim, sch, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
 int flux_attn_schedule(int32_t tiles, int32_t kv_tiles, int32_t num_cus, int32_t max_pieces, int32_t head_dim,
                        int32_t* whole_tiles, int32_t* split_tiles, int32_t* split, int32_t* grid) {
   if (!whole_tiles || !split_tiles || !split || !grid) return fail(FLUX_ATTN_INVALID_ARGUMENT, "output is NULL");
@@ -411,6 +553,10 @@ int flux_attn_destroy(flux_attn_plan* plan) {
   release_timing(plan);
   (void)hipFree(plan->part_o);
   (void)hipFree(plan->part_ml);
+  (void)hipFree(plan->qbar);
+  (void)hipFree(plan->kbar);
+  (void)hipFree(plan->kv_list);
+  (void)hipFree(plan->kv_count);
   hipError_t e1 = hipFree(plan->rope_table);
   hipError_t e2 = hipFree(plan->freq);
   delete plan;

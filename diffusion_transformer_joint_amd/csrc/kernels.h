@@ -24,6 +24,11 @@ struct AttnArgs {
   int split;
   float* part_o;          // [slot][256][D] un-normalized O of each partial
   float2* part_ml;        // [slot][256] (running max in the exp2 domain, row sum)
+  // Tile-sparse launches only: kept 64-key tiles of each 256-row query tile,
+  // ascending, kv_list[tile * list_stride + i] for i < kv_count[tile].
+  const int* kv_list;
+  const int* kv_count;
+  int list_stride;
 };
 
 // How one launch covers T query tiles of 256 rows with K/V ranges of n_kv
@@ -65,5 +70,17 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch
 // Exact merge of split partials: O = sum_i 2^(m_i - m) O_i / sum_i 2^(m_i - m) l_i.
 hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream);
 hipError_t launch_attn_fp8(const Fp8Args& a, int head_dim, const Schedule& sch, hipStream_t stream);
+
+// Tile-sparse support (block_sparse.hip).  Means of the rotated rows of x over
+// tiles of `tile` tokens: fp32 [B][H][ceil(N/tile)][D].
+hipError_t launch_tile_means(const uint16_t* x, const float2* rope, float* out, int n_tokens, int batch_tokens,
+                             int heads, int batch, int head_dim, int tile, hipStream_t stream);
+// Mask rows (b, h, query tile) of pooled scores c * <qbar, kbar> against the
+// threshold row max + log2_tau: uint8 [rows][KT].
+hipError_t launch_block_select(const float* qbar, const float* kbar, uint8_t* mask, int rows, int QT, int KT,
+                               int head_dim, float c, float log2_tau, hipStream_t stream);
+// Kept key tiles of each mask row (ascending) into list[row * stride + i], count[row].
+hipError_t launch_mask_to_list(const uint8_t* mask, int* list, int* count, int rows, int KT, int stride,
+                               hipStream_t stream);
 
 }  // namespace flux

@@ -80,6 +80,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flux_attn_timing_enable": ([_vp, _i32], ctypes.c_int),
         "flux_attn_schedule": ([_i32, _i32, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p], ctypes.c_int),
         "flux_attn_timing_read": ([_vp, ctypes.POINTER(ctypes.c_float), _i32, _i32p], ctypes.c_int),
+        "flux_attn_block_mask": ([_vp, _vp, _vp, _i32p, _i32, _vp, ctypes.c_float, _vp, _vp], ctypes.c_int),
+        "flux_attn_forward_sparse": ([_vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -199,6 +201,68 @@ class Plan:
         check(self._lib.flux_attn_forward(self._handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), sp,
                                           segs, len(segment_tokens), pos_ids.data_ptr(), out.data_ptr(),
                                           _MODES[mode], stream.cuda_stream), "forward")
+        return out
+
+    def _check_qkv(self, q, k, v, segment_tokens, pos_ids):
+        import torch
+        if self._handle is None:
+            raise FluxAttnError(INVALID_ARGUMENT, "plan is closed")
+        for name, t in (("q", q), ("k", k), ("v", v), ("pos_ids", pos_ids)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise FluxAttnError(INVALID_ARGUMENT, f"{name} must be a contiguous device tensor")
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if t.dtype != torch.bfloat16:
+                raise FluxAttnError(INVALID_ARGUMENT, f"{name} has dtype {t.dtype}, expected bfloat16")
+        if pos_ids.dtype != torch.int32:
+            raise FluxAttnError(INVALID_ARGUMENT, "pos_ids must be int32")
+        n = int(sum(segment_tokens))
+        c = self.config
+        shape = (c.batch, n, c.num_heads, c.head_dim)
+        if tuple(q.shape) != shape or tuple(k.shape) != shape or tuple(v.shape) != shape:
+            raise FluxAttnError(INVALID_ARGUMENT, f"q/k/v must have shape {shape}")
+        if tuple(pos_ids.shape) != (n, 3):
+            raise FluxAttnError(INVALID_ARGUMENT, f"pos_ids must have shape {(n, 3)}")
+        return n, shape
+
+    def mask_shape(self, n_tokens: int) -> tuple:
+        """Shape of a tile mask: [B, H, ceil(N/256), ceil(N/64)]."""
+        c = self.config
+        return (c.batch, c.num_heads, (n_tokens + 255) // 256, (n_tokens + 63) // 64)
+
+    def block_mask(self, q, k, segment_tokens: Sequence[int], pos_ids, tau: float, mask=None, stream=None):
+        """Tile mask of the pooled-score rule (uint8 [B, H, QT, KT]) for threshold tau."""
+        import torch
+        n, _ = self._check_qkv(q, k, k, segment_tokens, pos_ids)
+        ms = self.mask_shape(n)
+        if mask is None:
+            mask = torch.empty(ms, dtype=torch.uint8, device=q.device)
+        elif tuple(mask.shape) != ms or mask.dtype != torch.uint8 or not mask.is_contiguous():
+            raise FluxAttnError(INVALID_ARGUMENT, f"mask must be a contiguous uint8 tensor of shape {ms}")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        segs = _i32_array(segment_tokens)
+        check(self._lib.flux_attn_block_mask(self._handle, q.data_ptr(), k.data_ptr(), segs, len(segment_tokens),
+                                             pos_ids.data_ptr(), float(tau), mask.data_ptr(), stream.cuda_stream),
+              "block_mask")
+        return mask
+
+    def forward_sparse(self, q, k, v, segment_tokens: Sequence[int], pos_ids, mask, out=None, stream=None):
+        """Attention over the kept tiles of ``mask`` (uint8 [B, H, QT, KT]).  Returns out."""
+        import torch
+        n, shape = self._check_qkv(q, k, v, segment_tokens, pos_ids)
+        ms = self.mask_shape(n)
+        if tuple(mask.shape) != ms or mask.dtype != torch.uint8 or not mask.is_cuda or not mask.is_contiguous():
+            raise FluxAttnError(INVALID_ARGUMENT, f"mask must be a contiguous uint8 device tensor of shape {ms}")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
+        elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+            raise FluxAttnError(INVALID_ARGUMENT, f"out must be a contiguous bf16 tensor of shape {shape}")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        segs = _i32_array(segment_tokens)
+        check(self._lib.flux_attn_forward_sparse(self._handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), segs,
+                                                 len(segment_tokens), pos_ids.data_ptr(), mask.data_ptr(),
+                                                 out.data_ptr(), stream.cuda_stream), "forward_sparse")
         return out
 
     def timing_enable(self, capacity: int) -> None:

@@ -58,6 +58,11 @@ class Workload:
     fp8: bool
     seed: int
     description: str
+    # Share of a per-(batch, head) direction u common to all of Q and K:
+    # q = sigma (a u + sqrt(1 - a^2) z).  With a > 0 the rotary embedding makes
+    # scores depend mostly on relative position (local attention).  0: plain
+    # Gaussian Q and K.
+    coherence: float = 0.0
 
     @property
     def tokens(self) -> int:
@@ -109,6 +114,9 @@ WORKLOADS: Dict[str, Workload] = {
                  "2048^2 with two 1024^2 references: 512 + 16,384 + 2x4,096 tokens (25,088)"),
         Workload("gen4k_fp8", 1, 24, 128, (_text(512), _img(256, 256)), 0.5, True, 5,
                  "4K generation, e4m3 Q/K/V with per-head scales: 512 + 256x256 tokens (66,048)"),
+        Workload("edit1024_local", 1, 24, 128, (_text(512), _img(64, 64), _ref(1, 64, 64)), 1.5, False, 6,
+                 "edit-call tokens (8,704) with position-local attention (sigma 1.5; Q and K share a "
+                 "per-head direction, coherence 0.9): input for tile-sparse attention", 0.9),
     ]
 }
 
@@ -147,10 +155,10 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _draw(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
-    x = rng.standard_normal(shape, dtype=np.float32)
+def _round(x: np.ndarray, sigma: float) -> np.ndarray:
+    """sigma * x (float32) rounded to bf16 bits."""
     if sigma != 1.0:
-        x *= np.float32(sigma)
+        x = x * np.float32(sigma)
     return f32_to_bf16_bits(x)
 
 
@@ -193,9 +201,16 @@ def make_inputs(w: Workload, seed: Optional[int] = None, sigma: Optional[float] 
     sigma = w.sigma if sigma is None else sigma
     rng = np.random.Generator(np.random.PCG64(seed))
     shape = (w.batch, w.tokens, w.heads, w.head_dim)
-    q = _draw(rng, shape, sigma)
-    k = _draw(rng, shape, sigma)
-    v = _draw(rng, shape, sigma)
+    zq = rng.standard_normal(shape, dtype=np.float32)
+    zk = rng.standard_normal(shape, dtype=np.float32)
+    zv = rng.standard_normal(shape, dtype=np.float32)
+    if w.coherence:
+        a = np.float32(w.coherence)
+        b = np.float32(np.sqrt(1.0 - w.coherence * w.coherence))
+        u = rng.standard_normal((w.batch, 1, w.heads, w.head_dim), dtype=np.float32)
+        zq = a * u + b * zq
+        zk = a * u + b * zk
+    q, k, v = (_round(z, sigma) for z in (zq, zk, zv))
     pos = position_ids(w.segments)
     scales = None
     if w.fp8:

@@ -95,7 +95,8 @@ int flux_attn_validate_forward(const flux_attn_config* cfg, const void* q, const
 
 /* Creates a plan on the current HIP device: validates cfg and allocates the
  * plan's device workspace once (RoPE table of max_tokens x head_dim/2 float2,
- * split-K/V partials, counters).  *out receives the plan, or NULL on error. */
+ * split-K/V partials; for bf16 plans also the tile-sparse tile means and
+ * kept-tile lists).  *out receives the plan, or NULL on error. */
 int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out);
 
 /* Runs joint (or segment-local) RoPE attention asynchronously on hip_stream
@@ -116,6 +117,37 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
                       const float* qkv_scale, const int32_t* segment_tokens,
                       int32_t num_segments, const int32_t* pos_ids, void* out,
                       int32_t mode, void* hip_stream);
+
+/* Tile-sparse attention: skipping the work for less important token pairs by
+ * a sparsity threshold tau ("Optimizing FLUX 3 Image Klein inference on NVIDIA
+ * Blackwell GPUs", How it works; What you can do: tau).  The granularity and
+ * importance measure are this library's reading of that passage:
+ *   query tiles of 256 tokens x key tiles of 64 tokens of the joint sequence,
+ *   QT = ceil(N / 256), KT = ceil(N / 64) (last tiles may be partial);
+ *   mask: device uint8 [batch][num_heads][QT][KT], nonzero = the query tile
+ *   attends to the key tile.
+ * Both calls need a bf16 plan (FLUX_ATTN_UNSUPPORTED otherwise), take q, k, v,
+ * segment_tokens and pos_ids as forward() does (joint sequence), run
+ * asynchronously on hip_stream and share the plan's workspace (one call at a
+ * time per plan). */
+
+/* Writes the mask of the pooled-score rule: the pooled score of a tile pair is
+ * scale * log2(e) * <mean over the query tile of R(p_i) q_i, mean over the key
+ * tile of R(p_j) k_j> (fp32); a key tile is kept when its pooled score is at
+ * least the query tile's largest plus log2(tau), 0 < tau <= 1, so the largest
+ * is always kept.  mask is written in full. */
+int flux_attn_block_mask(flux_attn_plan* plan, const void* q, const void* k, const int32_t* segment_tokens,
+                         int32_t num_segments, const int32_t* pos_ids, float tau, uint8_t* mask,
+                         void* hip_stream);
+
+/* Attention of each query over the keys of its query tile's kept key tiles:
+ * the exact softmax over those keys (the others are left out); a query tile
+ * that keeps no key tile gets 0.  mask may come from flux_attn_block_mask or
+ * from the caller.  out is fully overwritten.  Timing pairs are recorded as
+ * for forward(). */
+int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k, const void* v,
+                             const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids,
+                             const uint8_t* mask, void* out, void* hip_stream);
 
 /* Kernel timing.  flux_attn_timing_enable(plan, capacity) with capacity > 0
  * creates capacity pairs of HIP events (capacity <= 4096); every following

@@ -7,9 +7,24 @@ from diffusion_transformer_joint_amd import inputs as I
 
 def test_workload_token_counts():
     n = {k: w.tokens for k, w in I.WORKLOADS.items()}
-    assert n == {"tiny": 80, "t2i1024": 4608, "edit1024": 8704, "gen2048r2": 25088, "gen4k_fp8": 66048}
+    assert n == {"tiny": 80, "t2i1024": 4608, "edit1024": 8704, "gen2048r2": 25088, "gen4k_fp8": 66048,
+                 "edit1024_local": 8704}
     assert I.WORKLOADS["edit1024"].segment_tokens == [512, 4096, 4096]
     assert I.WORKLOADS["gen2048r2"].segment_tokens == [512, 16384, 4096, 4096]
+
+
+def test_coherence_zero_keeps_draws_and_positive_shares_a_direction():
+    w = I.custom_workload("c", 1, 2, 64, [I.Segment("text", 300)], sigma=1.0)
+    a = I.make_inputs(w)
+    b = I.make_inputs(I.Workload(w.name, w.batch, w.heads, w.head_dim, w.segments, w.sigma, w.fp8, w.seed,
+                                 w.description, 0.0))
+    assert a.sha256() == b.sha256()
+    c = I.make_inputs(I.Workload(w.name, w.batch, w.heads, w.head_dim, w.segments, w.sigma, w.fp8, w.seed,
+                                 w.description, 0.9))
+    np.testing.assert_array_equal(c.v, a.v)          # V is not shared
+    q, k = I.bf16_bits_to_f32(c.q), I.bf16_bits_to_f32(c.k)
+    cos = (q * k).sum(-1) / np.linalg.norm(q, axis=-1) / np.linalg.norm(k, axis=-1)
+    assert 0.7 < cos.mean() < 0.9                    # a^2 = 0.81 of the energy is common
 
 
 def test_axes_split():
