@@ -83,6 +83,12 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     if constexpr (SPARSE) return p < kv1 ? kvlist[p] : n_tiles;
     else return p;
   };
+  // In the main loop a sparse range reads its list entries through vector
+  // loads two iterations ahead (a scalar load would make the loop's LDS waits
+  // drain completely): kv_roll = tiles at positions t, t+1, t+2.
+  int kv_roll[3] = {0, 0, 0};
+  uint32_t kv_ahead = 0;  // list entry of position t+3, loaded during iteration t
+  const __amdgpu_buffer_rsrc_t rlist = make_rsrc(kvlist, SPARSE ? (uint32_t)kv1 * 4u : 0u);
   const int qt = tile % a.q_tiles;
   const int bh = tile / a.q_tiles;
   const int h = bh % H, b = bh / H;
@@ -345,7 +351,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm[(i + 1) & 1];  // V(t-1)
     FLUX_LDS char* kw = (FLUX_LDS char*)ksm[(i + 1) & 1];              // K(t+1)
     FLUX_LDS char* vw = (FLUX_LDS char*)vsm[i & 1];                    // V(t)
-    const int kt0 = kvt(t) * C::BN;
+    const int kt0 = (SPARSE ? kv_roll[0] : t) * C::BN;
     // MFMA j < NK: S(t), K fragment j; NK <= j < NL: PV(t-1), V fragment j - NK.
     constexpr int NK = 2 * C::KSTEPS, NL = NK + 4 * C::DB;
     auto ld = [&](int j) -> u32x4 {
@@ -398,8 +404,9 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
         constexpr int p = j == VST0 ? 0 : 1;
         lds_write_b128(vw + v_off<D>(st_row0 + p * C::RPP, st_chunk), vraw[p]);
       }
-      if constexpr (j == LVS) load_v(kvt(t + 1) * C::BN);
-      if constexpr (j == LKS) load_k(kvt(t + 2) * C::BN);
+      if constexpr (SPARSE && j == 0) kv_ahead = buffer_load_b32(rlist, (uint32_t)(t + 3) * 4u);
+      if constexpr (j == LVS) load_v((SPARSE ? kv_roll[1] : t + 1) * C::BN);
+      if constexpr (j == LKS) load_k((SPARSE ? kv_roll[2] : t + 2) * C::BN);
       if constexpr (j >= NK) {
         constexpr int v = j - NK;
         if (LAST && v == 0) mask(kt0, 0, s0);
@@ -432,11 +439,21 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
       pp[3] = make_p(s1, 1, b);
     }
     lsum += b;
+    if constexpr (SPARSE) {
+      kv_roll[0] = kv_roll[1];
+      kv_roll[1] = kv_roll[2];
+      kv_roll[2] = t + 3 < kv1 ? __builtin_amdgcn_readfirstlane((int)kv_ahead) : n_tiles;
+    }
     __syncthreads();
   };
 
   // positions before full_end hold full tiles; the last one may be ragged
   const int full_end = (N % C::BN != 0 && kvt(kv1 - 1) == n_tiles - 1) ? kv1 - 1 : kv1;
+  if constexpr (SPARSE) {
+    kv_roll[0] = kvt(kv0 + 1);
+    kv_roll[1] = kvt(kv0 + 2);
+    kv_roll[2] = kvt(kv0 + 3);
+  }
   if (kv0 < full_end) {
     step_first(std::false_type{});
     for (int t = kv0 + 1; t < full_end; ++t) step_main(t, std::false_type{});
