@@ -292,7 +292,7 @@ def main():
         "frac_bf16_peak": round(main_run["tflops"] / BF16_PEAK, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_bf16_kernel<128>", "kernel_ms_avg": round(main_run["kernel_ms_avg"], 4),
+                     "kernel": "attn_fwd_bf16_kernel<128, false>", "kernel_ms_avg": round(main_run["kernel_ms_avg"], 4),
                      "flops_per_launch": main_run["flops"]},
         "extra": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in extra],
     }

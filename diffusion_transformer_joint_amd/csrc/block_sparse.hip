@@ -83,17 +83,25 @@ __global__ __launch_bounds__(256) void block_select_kernel(const float* __restri
   for (int kt = threadIdx.x; kt < KT; kt += 256) mask[(size_t)row * KT + kt] = sc[kt] >= thr ? 1 : 0;
 }
 
-// Kept key tiles of each mask row, ascending, and their count.
-__global__ void mask_to_list_kernel(const uint8_t* __restrict__ mask, int* __restrict__ list,
-                                    int* __restrict__ count, int rows, int KT, int stride) {
-  const int row = blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= rows) return;
+// Kept key tiles of each mask row, ascending, and their count: one wave per
+// row, 64 entries per step, positions from a ballot prefix count.
+__global__ __launch_bounds__(256) void mask_to_list_kernel(const uint8_t* __restrict__ mask, int* __restrict__ list,
+                                                           int* __restrict__ count, int rows, int KT, int stride) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;  // whole waves leave together
   const uint8_t* m = mask + (size_t)row * KT;
   int* l = list + (size_t)row * stride;
   int n = 0;
-  for (int kt = 0; kt < KT; ++kt)
-    if (m[kt]) l[n++] = kt;
-  count[row] = n;
+  for (int k0 = 0; k0 < KT; k0 += 64) {
+    const int kt = k0 + lane;
+    const bool keep = kt < KT && m[kt] != 0;
+    const uint64_t bits = __ballot(keep);
+    const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0));
+    if (keep) l[n + before] = kt;
+    n += __popcll(bits);
+  }
+  if (lane == 0) count[row] = n;
 }
 
 hipError_t launch_tile_means(const uint16_t* x, const float2* rope, float* out, int n_tokens, int batch_tokens,
@@ -127,9 +135,8 @@ hipError_t launch_block_select(const float* qbar, const float* kbar, uint8_t* ma
 
 hipError_t launch_mask_to_list(const uint8_t* mask, int* list, int* count, int rows, int KT, int stride,
                                hipStream_t stream) {
-  const int threads = 256;
-  hipLaunchKernelGGL(mask_to_list_kernel, dim3((rows + threads - 1) / threads), dim3(threads), 0, stream, mask,
-                     list, count, rows, KT, stride);
+  hipLaunchKernelGGL(mask_to_list_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, mask, list, count, rows, KT,
+                     stride);
   return hipGetLastError();
 }
 
