@@ -13,11 +13,12 @@ What it computes (every function cites the passage it follows):
   * ``e4m3``       - decoding of OCP 8-bit e4m3 ("e4m3fn") codes from the
                      format's definition;
   * ``block_sparse`` - the tile-mask rule of threshold-sparse attention and
-                     exact attention over the kept tiles.
+                     exact attention over the kept tiles;
+  * ``backward``   - gradients (dq, dk, dv) of joint RoPE attention and the
+                     per-row log-sum-exp.
 
-Parity status: every function here is pinned by tests in
-``tests/test_oracle.py`` (closed forms, brute force, independent formulations,
-invariants).  What no test can pin is whether these conventions (pair layout,
+Parity status: every function here is pinned by tests in ``tests/test_oracle*.py``
+(closed forms, brute force, independent formulations, invariants).  What no test can pin is whether these conventions (pair layout,
 axis split, theta) are those of the real FLUX 3 model: no weights or model code
 are available, and both sides of every comparison use the same convention.
 """
@@ -28,3 +29,4 @@ from .softmax_attention import (softmax_rows, attention_from_scores, attention, 
 from .e4m3 import e4m3_decode, e4m3_table, dequantize  # noqa: F401
 from .inputs_fp64 import inputs_to_fp64  # noqa: F401
 from .block_sparse import tile_means, block_scores, block_mask, block_sparse_attention  # noqa: F401
+from .backward import rope_transpose, attention_lse, attention_backward  # noqa: F401
