@@ -12,7 +12,8 @@ resident in HBM before timing starts.  The 4,608-token text-to-image call, the
 66,048-token e4m3 call, the edit call in segment-local mode (each segment
 attending to itself), one GPU's share of the edit call under 8-way head
 sharding (3 heads, split K/V schedule), tile-sparse attention on edit-call
-tokens with position-local attention (thresholds 0.1 and 0.01) and, with
+tokens with position-local attention (thresholds 0.1 and 0.01), the attention
+backward (dq, dk, dv) of the edit call and, with
 --all, the 25,088-token call are reported as extra fields of the same JSON
 line.
 
@@ -180,6 +181,46 @@ def measure_sparse(workload, tau, steps, warmup):
     }
 
 
+def measure_backward(workload, steps, warmup):
+    """Training forward (with the row log-sum-exp) and the backward, timed apart.
+    Backward flops follow the usual count of five N x N x D products
+    (recomputed S, dP, dV, dQ, dK): 2.5 x the forward's."""
+    import numpy as np
+    import torch
+    from diffusion_transformer_joint_amd import inputs as I
+    from diffusion_transformer_joint_amd.flux_attn import Plan
+
+    w = I.WORKLOADS[workload]
+    inp = I.make_inputs(w)
+    dev = torch.device("cuda:0")
+    cv = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+    q, k, v = cv(inp.q), cv(inp.k), cv(inp.v)
+    pos = torch.from_numpy(inp.pos).to(dev)
+    rng = np.random.default_rng(99)
+    do = cv(I.f32_to_bf16_bits(rng.standard_normal(inp.q.shape, dtype=np.float32) * np.float32(0.5)))
+    plan = Plan(w.batch, w.heads, w.head_dim, w.tokens)
+    segs = w.segment_tokens
+    out, lse = plan.forward_lse(q, k, v, segs, pos)
+    for _ in range(warmup):
+        plan.backward(q, k, v, out, do, lse, segs, pos)
+    torch.cuda.synchronize()
+    plan.timing_enable(steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        plan.backward(q, k, v, out, do, lse, segs, pos)
+    e1.record()
+    torch.cuda.synchronize()
+    kernel_ms = plan.timing_read()
+    plan.close()
+    flops = 2.5 * w.flops()
+    kavg = sum(kernel_ms) / len(kernel_ms)
+    return {"workload": f"{w.name} (backward: dq, dk, dv)", "tokens": w.tokens, "heads": w.heads,
+            "head_dim": w.head_dim, "batch": w.batch, "dtype": "bf16", "flops": flops,
+            "ms_per_step": e0.elapsed_time(e1) / steps, "kernel_ms_avg": kavg,
+            "kernel_tflops": flops / (kavg * 1e-3) / 1e12, "frac_bf16_peak": flops / (kavg * 1e-3) / 1e12 / BF16_PEAK}
+
+
 def cpu_baseline(workload, rows_count):
     """The fp64 oracle, as it stands, on a bounded sample of query rows."""
     import numpy as np
@@ -263,6 +304,9 @@ def main():
             r["frac_mixed_ceiling"] = r["kernel_tflops"] / (2.0 / (1.0 / FP8_PEAK + 1.0 / BF16_PEAK))
         extra.append(r)
         log(f"{r['workload']}: {r['kernel_tflops']:.1f} TFLOP/s kernel")
+    r = measure_backward("edit1024", max(5, args.steps // 5), max(2, args.warmup // 2))
+    extra.append(r)
+    log(f"{r['workload']}: {r['kernel_ms_avg']:.3f} ms, {r['kernel_tflops']:.1f} TFLOP/s (2.5 x forward flops)")
     for tau in (0.1, 0.01):
         r = measure_sparse("edit1024_local", tau, max(5, args.steps // 2), max(2, args.warmup // 2))
         r["speedup_vs_dense_edit1024"] = main_run["kernel_ms_avg"] / r["kernel_ms_avg"]

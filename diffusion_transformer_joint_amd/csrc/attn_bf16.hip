@@ -487,6 +487,8 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   }
   // ---- epilogue: O = O^T / l, bf16, stored row-major.
   const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;  // 0: an empty tile-sparse range
+  if (a.lse != nullptr && g == 0 && qrow < N)
+    a.lse[((size_t)b * H + h) * N + qrow] = (m_ref + __builtin_log2f(ltot)) * 0.6931471805599453f;
   if (qrow < N) {
     uint16_t* orow = a.o + bat + (size_t)qrow * tok_stride + (size_t)h * D;
 #pragma unroll
@@ -530,6 +532,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     acc[4] += w * x1[0]; acc[5] += w * x1[1]; acc[6] += w * x1[2]; acc[7] += w * x1[3];
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;  // 0: no kept keys (tile-sparse)
+  if (a.lse != nullptr && d0 == 0)
+    a.lse[((size_t)b * a.heads + h) * a.n_tokens + row] = (m + __builtin_log2f(l)) * 0.6931471805599453f;
   u32x4 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);

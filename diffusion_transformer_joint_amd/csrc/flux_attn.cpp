@@ -67,6 +67,7 @@ struct flux_attn_plan {
   float* kbar = nullptr;         // [B][H][KT][D]
   int* kv_list = nullptr;        // [B*H*QT][KT]
   int* kv_count = nullptr;       // [B*H*QT]
+  float* dr = nullptr;           // backward: rowsum(dO * O), [B][H][N]
   int num_cus = 0;
   int max_pieces = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;  // kernel timing pairs
@@ -265,6 +266,7 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     if (e == hipSuccess) e = hipMalloc(&p->kbar, rows * kt * cfg->head_dim * sizeof(float));
     if (e == hipSuccess) e = hipMalloc(&p->kv_list, rows * qt * kt * sizeof(int));
     if (e == hipSuccess) e = hipMalloc(&p->kv_count, rows * qt * sizeof(int));
+    if (e == hipSuccess) e = hipMalloc(&p->dr, rows * cfg->max_tokens * sizeof(float));
   }
   if (e != hipSuccess) {
     (void)hipFree(p->rope_table);
@@ -275,6 +277,7 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     (void)hipFree(p->kbar);
     (void)hipFree(p->kv_list);
     (void)hipFree(p->kv_count);
+    (void)hipFree(p->dr);
     delete p;
     return hip_fail(e, "plan workspace");
   }
@@ -293,9 +296,11 @@ int flux_attn_get_config(const flux_attn_plan* plan, flux_attn_config* cfg) {
   return ok();
 }
 
-int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const void* v, const float* qkv_scale,
-                      const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
-                      int32_t mode, void* hip_stream) {
+namespace {
+
+int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void* v, const float* qkv_scale,
+                 const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
+                 int32_t mode, float* lse, void* hip_stream) {
   if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
   const flux_attn_config& c = plan->cfg;
   int st = flux_attn_validate_forward(&c, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out, mode);
@@ -344,6 +349,7 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
     a.c = scale * log2e;
     a.part_o = plan->part_o;
     a.part_ml = plan->part_ml;
+    a.lse = lse;
     if (c.dtype == FLUX_ATTN_FP8_E4M3) {
       flux::Fp8Args f{};
       f.q = static_cast<const uint8_t*>(q) + off * tok;
@@ -376,6 +382,93 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
     }
     e = flux::launch_attn_merge(a, c.head_dim, sch, stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const void* v, const float* qkv_scale,
+                      const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
+                      int32_t mode, void* hip_stream) {
+  return forward_impl(plan, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out, mode, nullptr,
+                      hip_stream);
+}
+
+int flux_attn_forward_lse(flux_attn_plan* plan, const void* q, const void* k, const void* v,
+                          const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
+                          float* lse, void* hip_stream) {
+  if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
+  if (plan->cfg.dtype != FLUX_ATTN_BF16) return fail(FLUX_ATTN_UNSUPPORTED, "the training forward needs a bf16 plan");
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "lse is NULL or misaligned");
+  return forward_impl(plan, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, out, FLUX_ATTN_JOINT, lse,
+                      hip_stream);
+}
+
+int flux_attn_backward(flux_attn_plan* plan, const void* q, const void* k, const void* v, const void* out,
+                       const void* dout, const float* lse, const int32_t* segment_tokens, int32_t num_segments,
+                       const int32_t* pos_ids, void* dq, void* dk, void* dv, void* hip_stream) {
+  if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
+  const flux_attn_config& c = plan->cfg;
+  if (c.dtype != FLUX_ATTN_BF16) return fail(FLUX_ATTN_UNSUPPORTED, "the backward needs a bf16 plan");
+  int st = flux_attn_validate_forward(&c, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, out,
+                                      FLUX_ATTN_JOINT);
+  if (st) return st;
+  if (!dout || !lse || !dq || !dk || !dv) return fail(FLUX_ATTN_INVALID_ARGUMENT, "a gradient pointer is NULL");
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "dout, dq, dk, dv must be 16-byte aligned and lse 4-byte aligned");
+  int n = 0;
+  for (int i = 0; i < num_segments; ++i) n += segment_tokens[i];
+  const size_t bytes = (size_t)c.batch * n * c.num_heads * c.head_dim * 2;
+  const void* ins[5] = {q, k, v, out, dout};
+  void* grads[3] = {dq, dk, dv};
+  for (int gi = 0; gi < 3; ++gi) {
+    for (int ii = 0; ii < 5; ++ii)
+      if (overlaps(grads[gi], bytes, ins[ii], bytes))
+        return fail(FLUX_ATTN_INVALID_ARGUMENT, "a gradient overlaps an input");
+    for (int gj = 0; gj < gi; ++gj)
+      if (overlaps(grads[gi], bytes, grads[gj], bytes))
+        return fail(FLUX_ATTN_INVALID_ARGUMENT, "dq, dk and dv overlap");
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan was created on device %d, current device is %d", plan->device, dev);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  e = flux::launch_rope_table(pos_ids, plan->freq, plan->rope_table, n, c.head_dim, c.rope_axes_dim[0],
+                              c.rope_axes_dim[1], stream);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  const float scale = c.softmax_scale > 0.0f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
+  flux::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<const uint16_t*>(out);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dr = plan->dr;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.rope = plan->rope_table;
+  a.n_tokens = n;
+  a.heads = c.num_heads;
+  a.batch = c.batch;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  const bool timed = plan->timing_used < (int)plan->ev_start.size();
+  if (timed) {
+    e = hipEventRecord(plan->ev_start[plan->timing_used], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  e = flux::launch_attn_bwd(a, c.head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  if (timed) {
+    e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    ++plan->timing_used;
   }
   return ok();
 }
@@ -557,6 +650,7 @@ int flux_attn_destroy(flux_attn_plan* plan) {
   (void)hipFree(plan->kbar);
   (void)hipFree(plan->kv_list);
   (void)hipFree(plan->kv_count);
+  (void)hipFree(plan->dr);
   hipError_t e1 = hipFree(plan->rope_table);
   hipError_t e2 = hipFree(plan->freq);
   delete plan;

@@ -29,6 +29,8 @@ struct AttnArgs {
   const int* kv_list;
   const int* kv_count;
   int list_stride;
+  // Optional: natural-log log-sum-exp of each row of scale * S, [B][H][N].
+  float* lse;
 };
 
 // How one launch covers T query tiles of 256 rows with K/V ranges of n_kv
@@ -67,6 +69,27 @@ hipError_t launch_rope_table(const int32_t* pos, const double* freq, float2* tab
                              int head_dim, int d0, int d1, hipStream_t stream);
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream);
+
+// Backward of the bf16 joint attention (attn_bwd.hip).
+struct BwdArgs {
+  const uint16_t* q;      // [B][N][H][D] bf16 bits (unrotated)
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;    // forward output
+  const uint16_t* dout;   // upstream gradient
+  const float* lse;       // [B][H][N] natural-log log-sum-exp of scale * S
+  float* dr;              // [B][H][N] workspace: rowsum(dout * out)
+  uint16_t* dq;           // [B][N][H][D] bf16
+  uint16_t* dk;
+  uint16_t* dv;
+  const float2* rope;     // [N][D/2] (cos, sin)
+  int n_tokens;
+  int heads;
+  int batch;
+  float c;                // scale * log2(e)
+  float scale;
+};
+hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, hipStream_t stream);
 // Exact merge of split partials: O = sum_i 2^(m_i - m) O_i / sum_i 2^(m_i - m) l_i.
 hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream);
 hipError_t launch_attn_fp8(const Fp8Args& a, int head_dim, const Schedule& sch, hipStream_t stream);

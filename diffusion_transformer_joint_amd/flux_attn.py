@@ -82,6 +82,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flux_attn_timing_read": ([_vp, ctypes.POINTER(ctypes.c_float), _i32, _i32p], ctypes.c_int),
         "flux_attn_block_mask": ([_vp, _vp, _vp, _i32p, _i32, _vp, ctypes.c_float, _vp, _vp], ctypes.c_int),
         "flux_attn_forward_sparse": ([_vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+        "flux_attn_forward_lse": ([_vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+        "flux_attn_backward": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp, _vp],
+                               ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -264,6 +267,48 @@ class Plan:
                                                  len(segment_tokens), pos_ids.data_ptr(), mask.data_ptr(),
                                                  out.data_ptr(), stream.cuda_stream), "forward_sparse")
         return out
+
+    def forward_lse(self, q, k, v, segment_tokens: Sequence[int], pos_ids, out=None, lse=None, stream=None):
+        """Joint forward that also returns the row log-sum-exp ([B, H, N] float32).  Returns (out, lse)."""
+        import torch
+        n, shape = self._check_qkv(q, k, v, segment_tokens, pos_ids)
+        c = self.config
+        if out is None:
+            out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
+        elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+            raise FluxAttnError(INVALID_ARGUMENT, f"out must be a contiguous bf16 tensor of shape {shape}")
+        ls = (c.batch, c.num_heads, n)
+        if lse is None:
+            lse = torch.empty(ls, dtype=torch.float32, device=q.device)
+        elif tuple(lse.shape) != ls or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise FluxAttnError(INVALID_ARGUMENT, f"lse must be a contiguous float32 tensor of shape {ls}")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        segs = _i32_array(segment_tokens)
+        check(self._lib.flux_attn_forward_lse(self._handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), segs,
+                                              len(segment_tokens), pos_ids.data_ptr(), out.data_ptr(),
+                                              lse.data_ptr(), stream.cuda_stream), "forward_lse")
+        return out, lse
+
+    def backward(self, q, k, v, out, dout, lse, segment_tokens: Sequence[int], pos_ids, stream=None):
+        """Gradients (dq, dk, dv) of the joint attention for upstream gradient dout."""
+        import torch
+        n, shape = self._check_qkv(q, k, v, segment_tokens, pos_ids)
+        c = self.config
+        for name, t in (("out", out), ("dout", dout)):
+            if tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+                raise FluxAttnError(INVALID_ARGUMENT, f"{name} must be a contiguous bf16 device tensor of shape {shape}")
+        if tuple(lse.shape) != (c.batch, c.num_heads, n) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise FluxAttnError(INVALID_ARGUMENT, "lse must be a contiguous float32 [B, H, N] tensor")
+        dq, dk, dv = (torch.empty(shape, dtype=torch.bfloat16, device=q.device) for _ in range(3))
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        segs = _i32_array(segment_tokens)
+        check(self._lib.flux_attn_backward(self._handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                           dout.data_ptr(), lse.data_ptr(), segs, len(segment_tokens),
+                                           pos_ids.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                           stream.cuda_stream), "backward")
+        return dq, dk, dv
 
     def timing_enable(self, capacity: int) -> None:
         """Record the attention kernel's duration for the next ``capacity`` forwards."""

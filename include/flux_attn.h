@@ -96,7 +96,8 @@ int flux_attn_validate_forward(const flux_attn_config* cfg, const void* q, const
 /* Creates a plan on the current HIP device: validates cfg and allocates the
  * plan's device workspace once (RoPE table of max_tokens x head_dim/2 float2,
  * split-K/V partials; for bf16 plans also the tile-sparse tile means and
- * kept-tile lists).  *out receives the plan, or NULL on error. */
+ * kept-tile lists and the backward's row sums).  *out receives the plan, or
+ * NULL on error. */
 int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out);
 
 /* Runs joint (or segment-local) RoPE attention asynchronously on hip_stream
@@ -117,6 +118,33 @@ int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const 
                       const float* qkv_scale, const int32_t* segment_tokens,
                       int32_t num_segments, const int32_t* pos_ids, void* out,
                       int32_t mode, void* hip_stream);
+
+/* Training: forward with the per-row log-sum-exp, and the backward.  The
+ * attention backward is the adjacent training workload (LoRA fine-tuning of
+ * the base model, "FLUX.3 Image Klein Brings 2-Second AI Image Generation to
+ * Diffusers", Summary); the pages give no formula, so these are the gradients
+ * of the operation above.  Both need a bf16 plan (FLUX_ATTN_UNSUPPORTED
+ * otherwise) and run joint attention over the whole sequence, asynchronously
+ * on hip_stream, one call at a time per plan.
+ *
+ * flux_attn_forward_lse: forward() (joint) that also writes
+ *   lse[b][h][i] = log sum_j exp(scale * <R(p_i) q_i, R(p_j) k_j>)
+ * (natural log, fp32, device [batch][num_heads][N]).
+ *
+ * flux_attn_backward: given q, k, v, the forward's out and lse, and the
+ * upstream gradient dout (all device, layouts as forward), writes dq, dk, dv
+ * (device [batch][N][num_heads][head_dim] bf16, fully overwritten) with
+ *   P = softmax rows of scale * S,  dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),
+ *   dq = R^T (scale dS K~),  dk = R^T (scale dS^T Q~)
+ * where Q~ = R q, K~ = R k and R^T rotates back by the negative angle.  The
+ * gradients must not overlap any input or each other.  Timing pairs (see
+ * below) bracket the backward kernels. */
+int flux_attn_forward_lse(flux_attn_plan* plan, const void* q, const void* k, const void* v,
+                          const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
+                          float* lse, void* hip_stream);
+int flux_attn_backward(flux_attn_plan* plan, const void* q, const void* k, const void* v, const void* out,
+                       const void* dout, const float* lse, const int32_t* segment_tokens, int32_t num_segments,
+                       const int32_t* pos_ids, void* dq, void* dk, void* dv, void* hip_stream);
 
 /* Tile-sparse attention: skipping the work for less important token pairs by
  * a sparsity threshold tau ("Optimizing FLUX 3 Image Klein inference on NVIDIA

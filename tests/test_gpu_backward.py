@@ -1,0 +1,96 @@
+"""GPU parity of the training forward (row log-sum-exp) and the backward.
+
+Oracle: oracle/backward.py (explicit fp64 gradients, pinned against torch
+autograd and finite differences on the CPU).  The upstream gradient is drawn
+by a seeded generator here; nothing from the GPU enters the oracle.
+
+Tolerance (derived from the arithmetic): the GPU rounds P and dS to bf16
+before the MFMAs and the gradients to bf16 at the end (each 2^-9 relative),
+and uses its own bf16 O for rowsum(dO O).  Gradients are sums over N terms of
+such rounded products, so their relative L2 error is a small multiple of the
+forward's; the bound used is relative L2 <= 1.5e-2 per gradient (three times
+the forward's 5e-3).  The log-sum-exp is m + log(l) with l the fp32 sum of the
+bf16-rounded p the forward multiplies V with (each within 2^-9 relative), so
+|lse - lse_exact| <= 2^-9 plus fp32 rounding: bound 2.5e-3.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from diffusion_transformer_joint_amd import inputs as I
+
+from gpu_helpers import custom, errors, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+S = I.Segment
+GRAD_REL_L2 = 1.5e-2
+
+
+def _dout(inp, seed):
+    rng = np.random.default_rng(seed)
+    return I.f32_to_bf16_bits(rng.standard_normal(inp.q.shape, dtype=np.float32) * np.float32(0.5))
+
+
+def _run(inp, dout_bits):
+    import torch
+    from diffusion_transformer_joint_amd.flux_attn import Plan
+    w = inp.workload
+    q, k, v, pos, _ = to_device(inp)
+    do = torch.from_numpy(dout_bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    with Plan(w.batch, w.heads, w.head_dim, w.tokens) as plan:
+        say(f"  HIP forward_lse + backward: {w.name} B={w.batch} N={w.tokens} H={w.heads} D={w.head_dim}")
+        out, lse = plan.forward_lse(q, k, v, inp.segment_tokens, pos)
+        dq, dk, dv = plan.backward(q, k, v, out, do, lse, inp.segment_tokens, pos)
+        torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    return f(out), lse.cpu().numpy().astype(np.float64), f(dq), f(dk), f(dv)
+
+
+CASES = [
+    ("bw_n300", 1, 2, 128, [S("text", 44), S("image", 16, 16)], 1.0),
+    ("bw_n1000", 1, 3, 128, [S("text", 40), S("image", 24, 40)], 0.5),
+    ("bw_b2_n257", 2, 2, 128, [S("text", 1), S("image", 16, 16)], 1.0),
+    ("bw_d64_n200", 1, 2, 64, [S("text", 8), S("image", 12, 16)], 1.0),
+    ("bw_n1", 1, 2, 128, [S("text", 1)], 1.0),
+]
+
+
+@pytest.mark.parametrize("name,batch,heads,d,segs,sigma", CASES, ids=[c[0] for c in CASES])
+def test_backward_against_oracle(name, batch, heads, d, segs, sigma):
+    inp = I.make_inputs(custom(name, heads, d, segs, batch=batch, sigma=sigma))
+    dob = _dout(inp, 77)
+    out, lse, dq, dk, dv = _run(inp, dob)
+    w = inp.workload
+    q, k, v = oracle.inputs_to_fp64(inp)
+    do = I.bf16_bits_to_f32(dob).astype(np.float64)
+    rq, rk, rv = oracle.attention_backward(q, k, v, inp.pos, w.axes_dim, do)
+    rl = oracle.attention_lse(q, k, inp.pos, w.axes_dim)
+    assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+    lerr = float(np.abs(lse - rl).max())
+    say(f"  {name}: lse max-abs {lerr:.2e}")
+    assert lerr < 2.5e-3
+    for gname, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        ma, rel = errors(got, ref)
+        say(f"  {name} {gname}: max-abs {ma:.3e} rel-L2 {rel:.3e} (|ref| max {np.abs(ref).max():.3e})")
+        if np.linalg.norm(ref) == 0.0:
+            assert ma < 1e-6
+        else:
+            assert rel <= GRAD_REL_L2, f"{name} {gname}: rel-L2 {rel:.3e}"
+
+
+def test_backward_edit1024_three_heads():
+    # The 8,704-token edit call at one GPU's 3-head share: full-size rows and
+    # columns, every query tile and key tile of the joint sequence.
+    import dataclasses
+    w = dataclasses.replace(I.WORKLOADS["edit1024"], heads=3, name="edit1024_3heads")
+    inp = I.make_inputs(w)
+    dob = _dout(inp, 78)
+    out, lse, dq, dk, dv = _run(inp, dob)
+    q, k, v = oracle.inputs_to_fp64(inp)
+    do = I.bf16_bits_to_f32(dob).astype(np.float64)
+    rq, rk, rv = oracle.attention_backward(q, k, v, inp.pos, w.axes_dim, do)
+    for gname, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        ma, rel = errors(got, ref)
+        say(f"  edit1024_3heads {gname}: max-abs {ma:.3e} rel-L2 {rel:.3e}")
+        assert rel <= GRAD_REL_L2
