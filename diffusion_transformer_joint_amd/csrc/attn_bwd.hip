@@ -9,20 +9,30 @@
 //   dQ~ = scale dS K~,  dK~ = scale dS^T Q~,  dq = R^T dQ~,  dk = R^T dK~
 // The forward's log-sum-exp (lse) is taken as given; P is recomputed.
 //
-// Two kernels, no atomics:
+// Four kernels, no atomics:
+//   attn_bwd_prep_kernel - one pass over the rows: Dr, and bf16 Q~ = R(q),
+//                          K~ = R(k) into workspace, so that the tiles the
+//                          other kernels stream (each is read once per
+//                          128-row workgroup of the head) need no rotation.
+//   attn_bwd_dkv_kernel  - key-stationary, one instance per gradient: dK
+//                          (S, dP, dS, dK~^T += Q~^T dS) and dV (S, P,
+//                          dV^T += dO^T P).  Splitting them recomputes S once
+//                          more (8 instead of 7 N x N x D products in all) but
+//                          lets each run two waves per SIMD: a fused kernel
+//                          needs both 32-key accumulators and both stationary
+//                          operands in registers, more than half the file.
 //   attn_bwd_dq_kernel   - query-stationary: a wave holds 32 queries (c Q~ and
-//                          dO as MFMA B operands); per 64-key tile it forms
+//                          dO as B operands); per 64-key tile it forms
 //                          S^T = K~ Q~^T and dP^T = V dO^T (lane = query), then
-//                          dS^T and dQ~^T += K~^T dS^T (K~ through the LDS
+//                          dS^T and dQ~^T += K~^T dS^T (K~ through the
 //                          transpose read).
-//   attn_bwd_dkdv_kernel - key-stationary: a wave holds 32 keys (c K~ and V as
-//                          B operands); per 64-query tile it forms S = Q~ K~^T
-//                          and dP = dO V^T (lane = key), then dV^T += dO^T P
-//                          and dK~^T += Q~^T dS (dO and Q~ through the
-//                          transpose read).
-// Both: 4 waves per workgroup (one per SIMD), 128 rows; the 32x32x16 bf16
-// MFMA with fp32 accumulation; RoPE applied while tiles are staged and
-// transposed back (R^T) on the gradients in the epilogue.
+// The streaming kernels: 4 waves per workgroup (32 rows each, 128 rows), two
+// workgroups per CU; the 32x32x16 bf16 MFMA with fp32 accumulation; 64-row
+// tiles stream from global memory straight into double-buffered LDS (buffer
+// loads with the LDS destination, issued one tile ahead, one barrier per
+// tile); the stationary operands are rotated from q, k in registers and the
+// gradients rotated back (R^T) in the epilogue; workgroups of one head are
+// kept on one XCD so that its L2 serves the streamed tiles.
 #include "attn_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -39,10 +49,21 @@ struct BwdCfg {
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
-  static constexpr int ROWB = 2 * D + 16;  // LDS bytes per staged row
+  static constexpr int ROWB = 2 * D;       // LDS bytes per staged row (unpadded)
   static constexpr int TILEB = T * ROWB;
   static constexpr int CH = T * CPR / NT;  // chunks per thread per staged tile
 };
+
+// Staged tiles are read both one row per lane (b128: a 16-lane phase reads 16
+// rows at one chunk) and transposed (ds_read_b64_tr_b16: a 32-lane phase reads
+// 4 consecutive rows x 64 bytes).  Chunk c of row r sits at chunk
+// c ^ swz(r) of the row; swz makes both patterns, and the 16-lane row writes,
+// touch every bank once.
+template <int D> __device__ __forceinline__ int swz(int r);
+template <> __device__ __forceinline__ int swz<128>(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// 128-byte rows: two rows per bank cycle, so bit 0 of the row already picks
+// the half; bits 1..3 pick the chunk within it.
+template <> __device__ __forceinline__ int swz<64>(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 // R^T on a pair: rotation by the negative angle.
 __device__ __forceinline__ void rot_back(float& x0, float& x1, float2 cs) {
@@ -52,44 +73,128 @@ __device__ __forceinline__ void rot_back(float& x0, float& x1, float2 cs) {
   x1 = b;
 }
 
+__device__ __forceinline__ f32x4 lds_read_f32x4(const FLUX_LDS float* p) {
+  return *(const FLUX_LDS f32x4*)p;
+}
+
+// Per-lane LDS offsets of the two read patterns of a staged tile (relative to
+// the tile and to the 32-row block; the block adds 32 * ROWB).
+template <int D>
+struct TileOffsets {
+  using C = BwdCfg<D>;
+  int row[C::KSTEPS];  // b128: row krow_perm(l32), chunk 2t + g
+  int tr[C::DB][2];    // transposed: rows 8(grp/2) + li/4 (+4), bytes 64 db + 32 (grp&1) + 8 (li&3)
+  __device__ __forceinline__ TileOffsets(int lane) {
+    const int g = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
+    const int r = krow_perm(l32), sw = swz<D>(r);
+#pragma unroll
+    for (int t = 0; t < C::KSTEPS; ++t) row[t] = r * C::ROWB + 16 * ((2 * t + g) ^ sw);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int rr = 8 * (grp >> 1) + (li >> 2) + 4 * hi, sr = swz<D>(rr);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const int cc = 4 * db + 2 * (grp & 1) + ((li & 3) >> 1);
+        tr[db][hi] = rr * C::ROWB + 16 * (cc ^ sr) + 8 * (li & 1);
+      }
+    }
+  }
+};
+
+// One streamed 64-row tile of one tensor, loaded straight into LDS
+// (buffer_load ... lds): each wave instruction fills 1 KB of LDS linearly
+// (16 bytes per lane at M0 + 16 lane), so the swizzle is applied to the
+// global side: the lane that fills LDS chunk pc of tile row r fetches
+// logical chunk pc ^ swz(r) of that row.
+template <int D>
+struct TileDma {
+  using C = BwdCfg<D>;
+  static constexpr int NI = C::TILEB / (C::NT * 16);  // instructions per tile
+  uint32_t voff[NI];
+  int wave_off;
+  __device__ __forceinline__ TileDma(int tid, uint32_t row_bytes) {
+    const int w = tid >> 6, l = tid & 63;
+    wave_off = __builtin_amdgcn_readfirstlane(w * 1024);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int p = i * C::NT * 16 + w * 1024 + 16 * l;
+      const int r = p / C::ROWB, pc = (p % C::ROWB) / 16;
+      voff[i] = (uint32_t)r * row_bytes + 16u * (uint32_t)(pc ^ swz<D>(r));
+    }
+  }
+  // rows from byte offset soff of the resource into the tile at lds
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t res, FLUX_LDS char* lds, uint32_t soff) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (FLUX_LDS void*)(lds + i * C::NT * 16 + wave_off), 16, voff[i],
+                                              soff, 0, 0);
+  }
+};
+
+// Wait for this wave's outstanding vector-memory loads (incl. LDS DMA).
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace
 
-// Dr[b][h][i] = sum_d dO[b][i][h][d] * O[b][i][h][d], fp32.
+// Per row (b, i, h): Dr = sum_d dO * O (fp32), bf16 R(q) and R(k).  One thread
+// per 16-byte chunk; the D/8 threads of a row reduce Dr by shuffles.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // (b, i, h)
+  constexpr int CPR = D / 8;
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = gid / CPR, cc = gid % CPR;  // row = (b N + i) H + h
   const int total = a.batch * a.n_tokens * a.heads;
-  if (idx >= total) return;
-  const int h = idx % a.heads, i = (idx / a.heads) % a.n_tokens, b = idx / (a.heads * a.n_tokens);
-  const size_t off = (size_t)idx * D;
+  const bool ok = row < total;  // whole rows are in or out: CPR divides the block
   float s = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 x = *(const u32x4*)(a.dout + off + 8 * c);
-    const u32x4 y = *(const u32x4*)(a.out + off + 8 * c);
+  int i = 0, h = 0, b = 0;
+  if (ok) {
+    h = row % a.heads;
+    i = (row / a.heads) % a.n_tokens;
+    b = row / (a.heads * a.n_tokens);
+    const size_t off = (size_t)row * D + 8 * cc;
+    const f32x4* rp = (const f32x4*)(a.rope + (size_t)i * (D / 2) + 4 * cc);
+    const f32x4 cs01 = rp[0], cs23 = rp[1];
+    *(u32x4*)(a.qr + off) = rope_chunk(global_load_b128(a.q + off), cs01, cs23);
+    *(u32x4*)(a.kr + off) = rope_chunk(global_load_b128(a.k + off), cs01, cs23);
+    const u32x4 x = global_load_b128(a.dout + off);
+    const u32x4 y = global_load_b128(a.out + off);
 #pragma unroll
     for (int e = 0; e < 4; ++e) s += bf16lo(x[e]) * bf16lo(y[e]) + bf16hi(x[e]) * bf16hi(y[e]);
   }
-  a.dr[((size_t)b * a.heads + h) * a.n_tokens + i] = s;
+#pragma unroll
+  for (int m = CPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, CPR);
+  if (ok && cc == 0) a.dr[((size_t)b * a.heads + h) * a.n_tokens + i] = s;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) char ksm[C::TILEB];  // K~ tile (rotated)
-  __shared__ __attribute__((aligned(16))) char vsm[C::TILEB];  // V tile
+  __shared__ __attribute__((aligned(16))) char ksm[2 * C::TILEB];  // K~ tiles (rotated)
+  __shared__ __attribute__((aligned(16))) char vsm[2 * C::TILEB];  // V tiles
   const int N = a.n_tokens, H = a.heads;
   const int q_tiles = (N + C::ROWS - 1) / C::ROWS;
-  const int qt = blockIdx.x % q_tiles, bh = blockIdx.x / q_tiles;
+  const int blk = xcd_tile_order(blockIdx.x, gridDim.x);
+  const int qt = blk % q_tiles, bh = blk / q_tiles;
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
+  const int g = lane >> 5, l32 = lane & 31;
   const size_t ts = (size_t)H * D;                          // elements between tokens
   const size_t base = (size_t)b * N * ts + (size_t)h * D;
   const float c = a.c;
 
-  // queries of this lane: c R(q) and dO as B fragments; lse2 and Dr
+  // K~ and V tiles stream straight from global memory into LDS; rows past N
+  // read as zero through the buffer range check
+  const uint32_t bytes = (uint32_t)(((size_t)(N - 1) * ts + D) * 2);
+  const __amdgpu_buffer_rsrc_t kres = make_rsrc(a.kr + base, bytes);
+  const __amdgpu_buffer_rsrc_t vres = make_rsrc(a.v + base, bytes);
+  const TileDma<D> dma(tid, (uint32_t)(ts * 2));
+  const uint32_t tile_bytes = (uint32_t)(C::T * ts * 2);
+  dma.issue(kres, (FLUX_LDS char*)ksm, 0);
+  dma.issue(vres, (FLUX_LDS char*)vsm, 0);
+
+  // queries of this lane: c R(q) and dO as B fragments; lse2 and Dr.  Rows
+  // past N carry zeros (finite p and dS; never stored).
   const int qrow = qt * C::ROWS + wave * 32 + l32;
   const bool qok = qrow < N;
   bf16x8 qf[C::KSTEPS], of[C::KSTEPS];
@@ -111,46 +216,28 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const size_t row_bh = ((size_t)b * H + h) * N;
   const float lse2 = qok ? a.lse[row_bh + qrow] * 1.4426950408889634f : 0.f;
   const float dr = qok ? a.dr[row_bh + qrow] : 0.f;
+  const TileOffsets<D> off(lane);
 
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = (f32x16){};
 
-  const int n_tiles = (N + C::T - 1) / C::T;
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int k0 = kt * C::T;
-    __syncthreads();
-    // stage K~ (rotated) and V rows of the tile; rows past N are zero
-#pragma unroll
-    for (int i = 0; i < C::CH; ++i) {
-      const int ch = tid + i * C::NT, r = ch / C::CPR, cc = ch % C::CPR;
-      u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-      f32x4 cs01 = {1.f, 0.f, 1.f, 0.f}, cs23 = {1.f, 0.f, 1.f, 0.f};
-      if (k0 + r < N) {
-        x = global_load_b128(a.k + base + (size_t)(k0 + r) * ts + 8 * cc);
-        y = global_load_b128(a.v + base + (size_t)(k0 + r) * ts + 8 * cc);
-        const f32x4* rp = (const f32x4*)(a.rope + (size_t)(k0 + r) * (D / 2) + 4 * cc);
-        cs01 = rp[0];
-        cs23 = rp[1];
-      }
-      lds_write_b128((FLUX_LDS char*)ksm + r * C::ROWB + 16 * cc, rope_chunk(x, cs01, cs23));
-      lds_write_b128((FLUX_LDS char*)vsm + r * C::ROWB + 16 * cc, y);
-    }
-    __syncthreads();
-    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm;
-    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm;
+  // one 64-key tile from LDS buffer BUF; MASK: the tile holds keys >= N
+  auto tile = [&](auto BUF, auto MASK, int k0) {
+    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm + decltype(BUF)::value * C::TILEB;
+    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm + decltype(BUF)::value * C::TILEB;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int krow = 32 * kb + krow_perm(l32);
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int t = 0; t < C::KSTEPS; ++t) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, lds_read_b128(kl + krow * C::ROWB + 16 * (2 * t + g)));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, lds_read_b128(vl + krow * C::ROWB + 16 * (2 * t + g)));
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, lds_read_b128(kl + 32 * kb * C::ROWB + off.row[t]));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, lds_read_b128(vl + 32 * kb * C::ROWB + off.row[t]));
         s = mfma_bf16(kf, qf[t], s);
         dp = mfma_bf16(vf, of[t], dp);
       }
-      // dS^T (keys x this lane's query), bf16, as the B operand of the next MFMA
+      // dS^T (keys x this lane's query), bf16, as the B operand of the next MFMA;
+      // element e holds key 32 kb + 16 (e / 8) + 8 g + e % 8 of the tile
       u32x4 dsf[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
@@ -160,8 +247,11 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int e = 8 * hh + 2 * i + u;
-            const int key = k0 + 32 * kb + 16 * (e >> 3) + 8 * g + (e & 7);
-            const float p = (key < N && qok) ? __builtin_amdgcn_exp2f(s[e] - lse2) : 0.f;
+            float p = __builtin_amdgcn_exp2f(s[e] - lse2);
+            if constexpr (decltype(MASK)::value) {
+              const int key = k0 + 32 * kb + 16 * (e >> 3) + 8 * g + (e & 7);
+              p = key < N ? p : 0.f;
+            }
             ds2[u] = p * (dp[e] - dr);
           }
           dsf[hh][i] = pack_bf16(ds2[0], ds2[1]);
@@ -169,17 +259,58 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       // dQ~^T += K~^T dS^T
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int krow0 = 32 * kb + 16 * hh + 8 * (grp >> 1) + (li >> 2);
+        const FLUX_LDS char* kb0 = kl + (32 * kb + 16 * hh) * C::ROWB;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const int d = 32 * db + 16 * (grp & 1) + 4 * (li & 3);
-          const u32x2 lo = lds_read_tr16(kl + krow0 * C::ROWB + 2 * d);
-          const u32x2 hi = lds_read_tr16(kl + (krow0 + 4) * C::ROWB + 2 * d);
+          const u32x2 lo = lds_read_tr16(kb0 + off.tr[db][0]);
+          const u32x2 hi = lds_read_tr16(kb0 + off.tr[db][1]);
           const u32x4 kk = {lo[0], lo[1], hi[0], hi[1]};
           acc[db] = mfma_bf16(__builtin_bit_cast(bf16x8, kk), __builtin_bit_cast(bf16x8, dsf[hh]), acc[db]);
         }
       }
     }
+  };
+
+  // Tiles alternate between the two LDS buffers; the next tile's loads are
+  // issued before the current tile's MFMAs and waited for at the barrier
+  // that ends it.  Pairs of full tiles run in the loop, so the accumulators
+  // stay in place; the last one or two tiles (one of them partial) follow.
+  const int n_tiles = (N + C::T - 1) / C::T;
+  const int n_full = N / C::T;  // tiles without keys past N
+  FLUX_LDS char* const k0s = (FLUX_LDS char*)ksm;
+  FLUX_LDS char* const k1s = (FLUX_LDS char*)ksm + C::TILEB;
+  FLUX_LDS char* const v0s = (FLUX_LDS char*)vsm;
+  FLUX_LDS char* const v1s = (FLUX_LDS char*)vsm + C::TILEB;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  dma_wait();
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= n_full; kt += 2) {
+    dma.issue(kres, k1s, (uint32_t)(kt + 1) * tile_bytes);
+    dma.issue(vres, v1s, (uint32_t)(kt + 1) * tile_bytes);
+    tile(B0{}, std::false_type{}, kt * C::T);
+    dma_wait();
+    __syncthreads();
+    if (kt + 2 < n_tiles) {
+      dma.issue(kres, k0s, (uint32_t)(kt + 2) * tile_bytes);
+      dma.issue(vres, v0s, (uint32_t)(kt + 2) * tile_bytes);
+    }
+    tile(B1{}, std::false_type{}, (kt + 1) * C::T);
+    dma_wait();
+    __syncthreads();
+  }
+  if (kt < n_full) {  // one full tile left (buffer 0), maybe a partial one after it
+    if (kt + 1 < n_tiles) {
+      dma.issue(kres, k1s, (uint32_t)(kt + 1) * tile_bytes);
+      dma.issue(vres, v1s, (uint32_t)(kt + 1) * tile_bytes);
+    }
+    tile(B0{}, std::false_type{}, kt * C::T);
+    dma_wait();
+    __syncthreads();
+    if (kt + 1 < n_tiles) tile(B1{}, std::true_type{}, (kt + 1) * C::T);
+  } else if (kt < n_tiles) {  // the partial tile (buffer 0)
+    tile(B0{}, std::true_type{}, kt * C::T);
   }
 
   // epilogue: dq = R^T (scale dQ~), bf16
@@ -204,28 +335,62 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_bwd_dkdv_kernel(BwdArgs a) {
+// Key-stationary gradients, one kernel per tensor (DK: dK, else dV).  A wave
+// holds 32 keys as B operands (c K~, and V for dK); per 64-query tile it forms
+// S = Q~ K~^T (and dP = dO V^T for dK) with lane = key, then
+//   dV^T += dO^T P           (dO through the transpose read), or
+//   dK~^T += Q~^T dS         (Q~ through the transpose read).
+// Queries past N stream in as zero rows with lse = Dr = 0: p = 1, dS = 0, and
+// their dO and Q~ rows are zero, so they add nothing.  Keys past N only touch
+// their own (unstored) accumulator columns.
+template <int D, bool DK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) char qsm[C::TILEB];  // Q~ tile (rotated)
-  __shared__ __attribute__((aligned(16))) char osm[C::TILEB];  // dO tile
-  __shared__ float lse_s[C::T], dr_s[C::T];
+  __shared__ __attribute__((aligned(16))) char qsm[2 * C::TILEB];  // Q~ tiles (rotated)
+  __shared__ __attribute__((aligned(16))) char osm[2 * C::TILEB];  // dO tiles
+  __shared__ __attribute__((aligned(16))) float lse_s[2 * C::T];   // natural-log lse of the tile's queries
+  __shared__ __attribute__((aligned(16))) float dr_s[2 * C::T];    // Dr of the tile's queries (dK)
   const int N = a.n_tokens, H = a.heads;
   const int k_tiles = (N + C::ROWS - 1) / C::ROWS;
-  const int kt = blockIdx.x % k_tiles, bh = blockIdx.x / k_tiles;
+  const int blk = xcd_tile_order(blockIdx.x, gridDim.x);
+  const int kt = blk % k_tiles, bh = blk / k_tiles;
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
+  const int g = lane >> 5, l32 = lane & 31;
   const size_t ts = (size_t)H * D;
   const size_t base = (size_t)b * N * ts + (size_t)h * D;
   const size_t row_bh = ((size_t)b * H + h) * N;
   const float c = a.c;
 
-  // keys of this lane: c R(k) and V as B fragments
+  const uint32_t bytes = (uint32_t)(((size_t)(N - 1) * ts + D) * 2);
+  const __amdgpu_buffer_rsrc_t qres = make_rsrc(a.qr + base, bytes);
+  const __amdgpu_buffer_rsrc_t ores = make_rsrc(a.dout + base, bytes);
+  const __amdgpu_buffer_rsrc_t lres = make_rsrc(a.lse + row_bh, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t dres = make_rsrc(a.dr + row_bh, (uint32_t)N * 4);
+  const TileDma<D> dma(tid, (uint32_t)(ts * 2));
+  const uint32_t tile_bytes = (uint32_t)(C::T * ts * 2);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  FLUX_LDS char* const qs[2] = {(FLUX_LDS char*)qsm, (FLUX_LDS char*)qsm + C::TILEB};
+  FLUX_LDS char* const os[2] = {(FLUX_LDS char*)osm, (FLUX_LDS char*)osm + C::TILEB};
+  FLUX_LDS float* const ls[2] = {(FLUX_LDS float*)lse_s, (FLUX_LDS float*)lse_s + C::T};
+  FLUX_LDS float* const dss[2] = {(FLUX_LDS float*)dr_s, (FLUX_LDS float*)dr_s + C::T};
+  // tile qt into buffer bf: Q~ and dO rows, lse (wave 0) and Dr (wave 1, dK)
+  auto issue = [&](int bf, int qt) {
+    dma.issue(qres, qs[bf], (uint32_t)qt * tile_bytes);
+    dma.issue(ores, os[bf], (uint32_t)qt * tile_bytes);
+    if (wv == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lres, (FLUX_LDS void*)ls[bf], 4, 4u * lane, (uint32_t)qt * C::T * 4, 0, 0);
+    if (DK && wv == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(dres, (FLUX_LDS void*)dss[bf], 4, 4u * lane, (uint32_t)qt * C::T * 4, 0,
+                                              0);
+  };
+  issue(0, 0);
+
+  // keys of this lane: c R(k) (and V) as B fragments
   const int krow = kt * C::ROWS + wave * 32 + l32;
   const bool kok = krow < N;
-  bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
+  bf16x8 kf[C::KSTEPS], vf[DK ? C::KSTEPS : 1];
 #pragma unroll
   for (int t = 0; t < C::KSTEPS; ++t) {
     const int d0 = 16 * t + 8 * g;
@@ -233,102 +398,101 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     f32x4 cs01 = {1.f, 0.f, 1.f, 0.f}, cs23 = {1.f, 0.f, 1.f, 0.f};
     if (kok) {
       x = global_load_b128(a.k + base + (size_t)krow * ts + d0);
-      y = global_load_b128(a.v + base + (size_t)krow * ts + d0);
+      if constexpr (DK) y = global_load_b128(a.v + base + (size_t)krow * ts + d0);
       const f32x4* rp = (const f32x4*)(a.rope + (size_t)krow * (D / 2) + d0 / 2);
       cs01 = rp[0];
       cs23 = rp[1];
     }
     kf[t] = __builtin_bit_cast(bf16x8, rope_chunk_scaled(x, cs01, cs23, c));
-    vf[t] = __builtin_bit_cast(bf16x8, y);
+    if constexpr (DK) vf[t] = __builtin_bit_cast(bf16x8, y);
   }
+  const TileOffsets<D> off(lane);
 
-  f32x16 dv[C::DB], dk[C::DB];
+  f32x16 acc[C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    dv[db] = (f32x16){};
-    dk[db] = (f32x16){};
-  }
+  for (int db = 0; db < C::DB; ++db) acc[db] = (f32x16){};
 
-  const int n_q = (N + C::T - 1) / C::T;
-  for (int qt = 0; qt < n_q; ++qt) {
-    const int q0 = qt * C::T;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < C::CH; ++i) {
-      const int ch = tid + i * C::NT, r = ch / C::CPR, cc = ch % C::CPR;
-      u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-      f32x4 cs01 = {1.f, 0.f, 1.f, 0.f}, cs23 = {1.f, 0.f, 1.f, 0.f};
-      if (q0 + r < N) {
-        x = global_load_b128(a.q + base + (size_t)(q0 + r) * ts + 8 * cc);
-        y = global_load_b128(a.dout + base + (size_t)(q0 + r) * ts + 8 * cc);
-        const f32x4* rp = (const f32x4*)(a.rope + (size_t)(q0 + r) * (D / 2) + 4 * cc);
-        cs01 = rp[0];
-        cs23 = rp[1];
-      }
-      lds_write_b128((FLUX_LDS char*)qsm + r * C::ROWB + 16 * cc, rope_chunk(x, cs01, cs23));
-      lds_write_b128((FLUX_LDS char*)osm + r * C::ROWB + 16 * cc, y);
-    }
-    if (tid < C::T) {
-      const bool ok = q0 + tid < N;
-      lse_s[tid] = ok ? a.lse[row_bh + q0 + tid] * 1.4426950408889634f : INFINITY;  // past N: p = 0
-      dr_s[tid] = ok ? a.dr[row_bh + q0 + tid] : 0.f;
-    }
-    __syncthreads();
-    const FLUX_LDS char* ql = (const FLUX_LDS char*)qsm;
-    const FLUX_LDS char* ol = (const FLUX_LDS char*)osm;
+  auto tile = [&](auto BUF) {
+    constexpr int bf = decltype(BUF)::value;
+    const FLUX_LDS char* ql = qs[bf];
+    const FLUX_LDS char* ol = os[bf];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int qr = 32 * qb + krow_perm(l32);
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int t = 0; t < C::KSTEPS; ++t) {
-        const bf16x8 qfr = __builtin_bit_cast(bf16x8, lds_read_b128(ql + qr * C::ROWB + 16 * (2 * t + g)));
-        const bf16x8 ofr = __builtin_bit_cast(bf16x8, lds_read_b128(ol + qr * C::ROWB + 16 * (2 * t + g)));
+        const bf16x8 qfr = __builtin_bit_cast(bf16x8, lds_read_b128(ql + 32 * qb * C::ROWB + off.row[t]));
         s = mfma_bf16(qfr, kf[t], s);
-        dp = mfma_bf16(ofr, vf[t], dp);
+        if constexpr (DK) {
+          const bf16x8 ofr = __builtin_bit_cast(bf16x8, lds_read_b128(ol + 32 * qb * C::ROWB + off.row[t]));
+          dp = mfma_bf16(ofr, vf[t], dp);
+        }
       }
-      // element e: query 32qb + 16(e/8) + 8g + e%8 of the tile, this lane's key
-      u32x4 pf[2], dsf[2];
+      // element e: query 32 qb + 16 (e / 8) + 8 g + e % 8 of the tile, this lane's key
+      u32x4 bfr[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh) {
+        const int q8 = 32 * qb + 16 * hh + 8 * g;
+        const f32x4 l0 = lds_read_f32x4(ls[bf] + q8), l1 = lds_read_f32x4(ls[bf] + q8 + 4);
+        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        float rv[8] = {};
+        if constexpr (DK) {
+          const f32x4 r0 = lds_read_f32x4(dss[bf] + q8), r1 = lds_read_f32x4(dss[bf] + q8 + 4);
+          const float t8[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) rv[i] = t8[i];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float p2[2], ds2[2];
+          float v2[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int e = 8 * hh + 2 * i + u;
-            const int ql_ = 32 * qb + 16 * (e >> 3) + 8 * g + (e & 7);
-            const float p = __builtin_amdgcn_exp2f(s[e] - lse_s[ql_]);
-            p2[u] = p;
-            ds2[u] = p * (dp[e] - dr_s[ql_]);
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(lv[2 * i + u], -1.4426950408889634f, s[e]));
+            v2[u] = DK ? p * (dp[e] - rv[2 * i + u]) : p;
           }
-          pf[hh][i] = pack_bf16(p2[0], p2[1]);
-          dsf[hh][i] = pack_bf16(ds2[0], ds2[1]);
+          bfr[hh][i] = pack_bf16(v2[0], v2[1]);
         }
-      // dV^T += dO^T P,  dK~^T += Q~^T dS
+      }
+      // dV^T += dO^T P  or  dK~^T += Q~^T dS
+      const FLUX_LDS char* al = DK ? ql : ol;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = 32 * qb + 16 * hh + 8 * (grp >> 1) + (li >> 2);
+        const int r0 = (32 * qb + 16 * hh) * C::ROWB;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const int d = 32 * db + 16 * (grp & 1) + 4 * (li & 3);
-          const u32x2 olo = lds_read_tr16(ol + r0 * C::ROWB + 2 * d);
-          const u32x2 ohi = lds_read_tr16(ol + (r0 + 4) * C::ROWB + 2 * d);
-          const u32x2 qlo = lds_read_tr16(ql + r0 * C::ROWB + 2 * d);
-          const u32x2 qhi = lds_read_tr16(ql + (r0 + 4) * C::ROWB + 2 * d);
-          const u32x4 oo = {olo[0], olo[1], ohi[0], ohi[1]};
-          const u32x4 qq = {qlo[0], qlo[1], qhi[0], qhi[1]};
-          dv[db] = mfma_bf16(__builtin_bit_cast(bf16x8, oo), __builtin_bit_cast(bf16x8, pf[hh]), dv[db]);
-          dk[db] = mfma_bf16(__builtin_bit_cast(bf16x8, qq), __builtin_bit_cast(bf16x8, dsf[hh]), dk[db]);
+          const u32x2 lo = lds_read_tr16(al + r0 + off.tr[db][0]);
+          const u32x2 hi = lds_read_tr16(al + r0 + off.tr[db][1]);
+          const u32x4 aa = {lo[0], lo[1], hi[0], hi[1]};
+          acc[db] = mfma_bf16(__builtin_bit_cast(bf16x8, aa), __builtin_bit_cast(bf16x8, bfr[hh]), acc[db]);
         }
       }
     }
-  }
+  };
 
-  // epilogue: dk = R^T (scale dK~), dv, bf16
+  // double-buffered query tiles, as in the dq kernel (no partial-tile case:
+  // rows past N are zeros that add nothing)
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const int n_q = (N + C::T - 1) / C::T;
+  dma_wait();
+  __syncthreads();
+  int qt = 0;
+  for (; qt + 2 <= n_q; qt += 2) {
+    issue(1, qt + 1);
+    tile(B0{});
+    dma_wait();
+    __syncthreads();
+    if (qt + 2 < n_q) issue(0, qt + 2);
+    tile(B1{});
+    dma_wait();
+    __syncthreads();
+  }
+  if (qt < n_q) tile(B0{});
+
+  // epilogue: dk = R^T (scale dK~) or dv, bf16
   if (kok) {
-    uint16_t* krow_k = a.dk + base + (size_t)krow * ts;
-    uint16_t* krow_v = a.dv + base + (size_t)krow * ts;
+    uint16_t* orow = (DK ? a.dk : a.dv) + base + (size_t)krow * ts;
     const float2* rp = a.rope + (size_t)krow * (D / 2);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -337,34 +501,51 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         const int d = 32 * db + 8 * aa + 4 * g;
         float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = dk[db][4 * aa + e] * a.scale;
-        rot_back(x[0], x[1], rp[d / 2]);
-        rot_back(x[2], x[3], rp[d / 2 + 1]);
-        u32x2 w, wv;
+        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * aa + e];
+        if constexpr (DK) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] *= a.scale;
+          rot_back(x[0], x[1], rp[d / 2]);
+          rot_back(x[2], x[3], rp[d / 2 + 1]);
+        }
+        u32x2 w;
         w[0] = pack_bf16(x[0], x[1]);
         w[1] = pack_bf16(x[2], x[3]);
-        wv[0] = pack_bf16(dv[db][4 * aa + 0], dv[db][4 * aa + 1]);
-        wv[1] = pack_bf16(dv[db][4 * aa + 2], dv[db][4 * aa + 3]);
-        *(u32x2*)(krow_k + d) = w;
-        *(u32x2*)(krow_v + d) = wv;
+        *(u32x2*)(orow + d) = w;
       }
   }
 }
 
-hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, hipStream_t stream) {
-  const int total = a.batch * a.n_tokens * a.heads;
+// Explicit instantiations: without them hipcc does not emit the host launch
+// stubs of some of these kernels when they are launched from the template below.
+template __global__ void attn_bwd_prep_kernel<128>(BwdArgs);
+template __global__ void attn_bwd_prep_kernel<64>(BwdArgs);
+template __global__ void attn_bwd_dq_kernel<128>(BwdArgs);
+template __global__ void attn_bwd_dq_kernel<64>(BwdArgs);
+template __global__ void attn_bwd_dkv_kernel<128, true>(BwdArgs);
+template __global__ void attn_bwd_dkv_kernel<128, false>(BwdArgs);
+template __global__ void attn_bwd_dkv_kernel<64, true>(BwdArgs);
+template __global__ void attn_bwd_dkv_kernel<64, false>(BwdArgs);
+
+template <int D>
+static void launch_bwd_kernels(const BwdArgs& a, hipStream_t stream) {
+  const long long chunks = (long long)a.batch * a.n_tokens * a.heads * (D / 8);
   const int tiles = a.batch * a.heads * ((a.n_tokens + 127) / 128);
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(attn_bwd_prep_kernel<128>, dim3((total + 255) / 256), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(tiles), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(tiles), dim3(256), 0, stream, a);
-  } else if (head_dim == 64) {
-    hipLaunchKernelGGL(attn_bwd_prep_kernel<64>, dim3((total + 255) / 256), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(tiles), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(tiles), dim3(256), 0, stream, a);
-  } else {
+  hipLaunchKernelGGL(attn_bwd_prep_kernel<D>, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a);
+  void (*const dk_kernel)(BwdArgs) = attn_bwd_dkv_kernel<D, true>;
+  void (*const dv_kernel)(BwdArgs) = attn_bwd_dkv_kernel<D, false>;
+  hipLaunchKernelGGL(dk_kernel, dim3(tiles), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(dv_kernel, dim3(tiles), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(tiles), dim3(256), 0, stream, a);
+}
+
+hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, hipStream_t stream) {
+  if (head_dim == 128)
+    launch_bwd_kernels<128>(a, stream);
+  else if (head_dim == 64)
+    launch_bwd_kernels<64>(a, stream);
+  else
     return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

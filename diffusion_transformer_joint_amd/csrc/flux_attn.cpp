@@ -68,6 +68,8 @@ struct flux_attn_plan {
   int* kv_list = nullptr;        // [B*H*QT][KT]
   int* kv_count = nullptr;       // [B*H*QT]
   float* dr = nullptr;           // backward: rowsum(dO * O), [B][H][N]
+  uint16_t* rq = nullptr;        // backward: bf16 R(q), R(k), [B][N][H][D]
+  uint16_t* rk = nullptr;
   int num_cus = 0;
   int max_pieces = 0;
   std::vector<hipEvent_t> ev_start, ev_stop;  // kernel timing pairs
@@ -267,6 +269,9 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     if (e == hipSuccess) e = hipMalloc(&p->kv_list, rows * qt * kt * sizeof(int));
     if (e == hipSuccess) e = hipMalloc(&p->kv_count, rows * qt * sizeof(int));
     if (e == hipSuccess) e = hipMalloc(&p->dr, rows * cfg->max_tokens * sizeof(float));
+    const size_t elems = rows * cfg->max_tokens * cfg->head_dim;
+    if (e == hipSuccess) e = hipMalloc(&p->rq, elems * sizeof(uint16_t));
+    if (e == hipSuccess) e = hipMalloc(&p->rk, elems * sizeof(uint16_t));
   }
   if (e != hipSuccess) {
     (void)hipFree(p->rope_table);
@@ -278,6 +283,8 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     (void)hipFree(p->kv_list);
     (void)hipFree(p->kv_count);
     (void)hipFree(p->dr);
+    (void)hipFree(p->rq);
+    (void)hipFree(p->rk);
     delete p;
     return hip_fail(e, "plan workspace");
   }
@@ -449,6 +456,8 @@ int flux_attn_backward(flux_attn_plan* plan, const void* q, const void* k, const
   a.dout = static_cast<const uint16_t*>(dout);
   a.lse = lse;
   a.dr = plan->dr;
+  a.qr = plan->rq;
+  a.kr = plan->rk;
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
@@ -651,6 +660,8 @@ int flux_attn_destroy(flux_attn_plan* plan) {
   (void)hipFree(plan->kv_list);
   (void)hipFree(plan->kv_count);
   (void)hipFree(plan->dr);
+  (void)hipFree(plan->rq);
+  (void)hipFree(plan->rk);
   hipError_t e1 = hipFree(plan->rope_table);
   hipError_t e2 = hipFree(plan->freq);
   delete plan;

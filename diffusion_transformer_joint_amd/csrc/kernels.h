@@ -79,6 +79,8 @@ struct BwdArgs {
   const uint16_t* dout;   // upstream gradient
   const float* lse;       // [B][H][N] natural-log log-sum-exp of scale * S
   float* dr;              // [B][H][N] workspace: rowsum(dout * out)
+  uint16_t* qr;           // [B][N][H][D] workspace: bf16 R(q)
+  uint16_t* kr;           // [B][N][H][D] workspace: bf16 R(k)
   uint16_t* dq;           // [B][N][H][D] bf16
   uint16_t* dk;
   uint16_t* dv;

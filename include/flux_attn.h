@@ -96,7 +96,8 @@ int flux_attn_validate_forward(const flux_attn_config* cfg, const void* q, const
 /* Creates a plan on the current HIP device: validates cfg and allocates the
  * plan's device workspace once (RoPE table of max_tokens x head_dim/2 float2,
  * split-K/V partials; for bf16 plans also the tile-sparse tile means and
- * kept-tile lists and the backward's row sums).  *out receives the plan, or
+ * kept-tile lists, and the backward's row sums and rotated copies of q and k:
+ * 2 x batch x max_tokens x num_heads x head_dim bf16).  *out receives the plan, or
  * NULL on error. */
 int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out);
 
