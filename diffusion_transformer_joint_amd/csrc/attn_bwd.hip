@@ -134,6 +134,104 @@ struct TileDma {
 // Wait for this wave's outstanding vector-memory loads (incl. LDS DMA).
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+enum BwdKind { KIND_DK = 0, KIND_DV = 1, KIND_DQ = 2 };
+
+// One 64-row streamed tile against one wave's 32 stationary rows (lane =
+// stationary row), in two 32-row halves u.  Per half:
+//   S = A(ra) st0 and, except for dV, dP = A(rb) st1 (A: streamed rows from
+//   LDS, st: stationary B fragments; c is already in st0), element e of lane l
+//   holding streamed row 32 u + 16 (e / 8) + 8 (l / 32) + e % 8 of the tile;
+//   p = exp2(S - lse log2 e);  B = p (dV) or p (dP - Dr) (dK, dq), bf16;
+//   acc[db] += A(ta)^T B, A(ta) through the transpose read.
+// lse and Dr come per streamed row from LDS (dK, dV) or per lane (dq).  MASK
+// (dq): streamed rows at or past lim get p = 0.  LDS operands are read NPF
+// MFMAs ahead; the first reads of each phase are issued in the one before.
+template <int D, int KIND, bool MASK>
+__device__ __forceinline__ void tile_pass(const FLUX_LDS char* ra, const FLUX_LDS char* rb, const FLUX_LDS char* ta,
+                                          const FLUX_LDS float* lse_t, const FLUX_LDS float* dr_t, float lse_l,
+                                          float dr_l, int lim, const bf16x8* st0, const bf16x8* st1,
+                                          const TileOffsets<D>& off, int g, f32x16* acc) {
+  using C = BwdCfg<D>;
+  constexpr bool TWO = KIND != KIND_DV;  // dP needed
+  constexpr bool ROWSTATS = KIND != KIND_DQ;
+  constexpr int NPF = 2;
+  constexpr int OSTEPS = 2 * C::DB;      // output MFMAs per half: (hh, db)
+  constexpr float L2E = 1.4426950408889634f;
+  auto rrow = [&](const FLUX_LDS char* t, int u, int k) {
+    return __builtin_bit_cast(bf16x8, lds_read_b128(t + 32 * u * C::ROWB + off.row[k]));
+  };
+  auto rtr = [&](int u, int j) {
+    const int hh = j / C::DB, db = j % C::DB;
+    const FLUX_LDS char* p = ta + (32 * u + 16 * hh) * C::ROWB;
+    const u32x2 lo = lds_read_tr16(p + off.tr[db][0]);
+    const u32x2 hi = lds_read_tr16(p + off.tr[db][1]);
+    return __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+  };
+  bf16x8 pa[NPF], pb[NPF], pt[NPF];
+  static_for<0, NPF>([&](auto K) {
+    pa[K] = rrow(ra, 0, K);
+    if constexpr (TWO) pb[K] = rrow(rb, 0, K);
+  });
+  static_for<0, 2>([&](auto U) {
+    constexpr int u = decltype(U)::value;
+    f32x16 s = {}, dp = {};
+    f32x4 ls[4], ds[4];  // lse, Dr of rows 32 u + 16 hh + 8 g + 4 q + 0..3 at [2 hh + q]
+    static_for<0, C::KSTEPS>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      s = mfma_bf16(pa[k % NPF], st0[k], s);
+      if constexpr (TWO) dp = mfma_bf16(pb[k % NPF], st1[k], dp);
+      if constexpr (k + NPF < C::KSTEPS) {
+        pa[k % NPF] = rrow(ra, u, k + NPF);
+        if constexpr (TWO) pb[k % NPF] = rrow(rb, u, k + NPF);
+      } else {
+        constexpr int j = k + NPF - C::KSTEPS;
+        pt[j] = rtr(u, j);
+        if constexpr (ROWSTATS && j == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ls[q] = lds_read_f32x4(lse_t + 32 * u + 16 * (q >> 1) + 8 * g + 4 * (q & 1));
+        }
+        if constexpr (KIND == KIND_DK && j == NPF - 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ds[q] = lds_read_f32x4(dr_t + 32 * u + 16 * (q >> 1) + 8 * g + 4 * (q & 1));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    u32x4 bfr[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v2[2];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const int e = 8 * hh + 2 * i + w, r8 = 2 * i + w;  // row 32 u + 16 hh + 8 g + r8
+          const float lse = ROWSTATS ? ls[2 * hh + (r8 >> 2)][r8 & 3] : lse_l;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(lse, -L2E, s[e]));
+          if constexpr (MASK) p = 32 * u + 16 * hh + 8 * g + r8 < lim ? p : 0.f;
+          if constexpr (KIND == KIND_DV)
+            v2[w] = p;
+          else
+            v2[w] = p * (dp[e] - (ROWSTATS ? ds[2 * hh + (r8 >> 2)][r8 & 3] : dr_l));
+        }
+        bfr[hh][i] = pack_bf16(v2[0], v2[1]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, OSTEPS>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      acc[j % C::DB] = mfma_bf16(pt[j % NPF], __builtin_bit_cast(bf16x8, bfr[j / C::DB]), acc[j % C::DB]);
+      if constexpr (j + NPF < OSTEPS) {
+        pt[j % NPF] = rtr(u, j + NPF);
+      } else if constexpr (u == 0) {
+        constexpr int k = j + NPF - OSTEPS;  // first row operands of the second half
+        pa[k] = rrow(ra, 1, k);
+        if constexpr (TWO) pb[k] = rrow(rb, 1, k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+}
+
 }  // namespace
 
 // Per row (b, i, h): Dr = sum_d dO * O (fp32), bf16 R(q) and R(k).  One thread
@@ -166,15 +264,14 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
   if (ok && cc == 0) a.dr[((size_t)b * a.heads + h) * a.n_tokens + i] = s;
 }
 
+// dq of the 128 queries of workgroup tile blk; smem holds the K~ and V tile
+// buffers (4 x 64 rows).
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bwd_dq_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_dq(const BwdArgs& a, int blk, FLUX_LDS char* sm0, FLUX_LDS char* sm1) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) char ksm[2 * C::TILEB];  // K~ tiles (rotated)
-  __shared__ __attribute__((aligned(16))) char vsm[2 * C::TILEB];  // V tiles
+  // buffer b: K~ tile (rotated) at smb, V tile at smb + TILEB
   const int N = a.n_tokens, H = a.heads;
   const int q_tiles = (N + C::ROWS - 1) / C::ROWS;
-  const int blk = xcd_tile_order(blockIdx.x, gridDim.x);
   const int qt = blk % q_tiles, bh = blk / q_tiles;
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -190,8 +287,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t vres = make_rsrc(a.v + base, bytes);
   const TileDma<D> dma(tid, (uint32_t)(ts * 2));
   const uint32_t tile_bytes = (uint32_t)(C::T * ts * 2);
-  dma.issue(kres, (FLUX_LDS char*)ksm, 0);
-  dma.issue(vres, (FLUX_LDS char*)vsm, 0);
+  dma.issue(kres, sm0, 0);
+  dma.issue(vres, sm0 + C::TILEB, 0);
 
   // queries of this lane: c R(q) and dO as B fragments; lse2 and Dr.  Rows
   // past N carry zeros (finite p and dS; never stored).
@@ -214,7 +311,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     of[t] = __builtin_bit_cast(bf16x8, y);
   }
   const size_t row_bh = ((size_t)b * H + h) * N;
-  const float lse2 = qok ? a.lse[row_bh + qrow] * 1.4426950408889634f : 0.f;
+  const float lse = qok ? a.lse[row_bh + qrow] : 0.f;
   const float dr = qok ? a.dr[row_bh + qrow] : 0.f;
   const TileOffsets<D> off(lane);
 
@@ -224,51 +321,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 
   // one 64-key tile from LDS buffer BUF; MASK: the tile holds keys >= N
   auto tile = [&](auto BUF, auto MASK, int k0) {
-    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm + decltype(BUF)::value * C::TILEB;
-    const FLUX_LDS char* vl = (const FLUX_LDS char*)vsm + decltype(BUF)::value * C::TILEB;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, lds_read_b128(kl + 32 * kb * C::ROWB + off.row[t]));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, lds_read_b128(vl + 32 * kb * C::ROWB + off.row[t]));
-        s = mfma_bf16(kf, qf[t], s);
-        dp = mfma_bf16(vf, of[t], dp);
-      }
-      // dS^T (keys x this lane's query), bf16, as the B operand of the next MFMA;
-      // element e holds key 32 kb + 16 (e / 8) + 8 g + e % 8 of the tile
-      u32x4 dsf[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float ds2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int e = 8 * hh + 2 * i + u;
-            float p = __builtin_amdgcn_exp2f(s[e] - lse2);
-            if constexpr (decltype(MASK)::value) {
-              const int key = k0 + 32 * kb + 16 * (e >> 3) + 8 * g + (e & 7);
-              p = key < N ? p : 0.f;
-            }
-            ds2[u] = p * (dp[e] - dr);
-          }
-          dsf[hh][i] = pack_bf16(ds2[0], ds2[1]);
-        }
-      // dQ~^T += K~^T dS^T
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const FLUX_LDS char* kb0 = kl + (32 * kb + 16 * hh) * C::ROWB;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const u32x2 lo = lds_read_tr16(kb0 + off.tr[db][0]);
-          const u32x2 hi = lds_read_tr16(kb0 + off.tr[db][1]);
-          const u32x4 kk = {lo[0], lo[1], hi[0], hi[1]};
-          acc[db] = mfma_bf16(__builtin_bit_cast(bf16x8, kk), __builtin_bit_cast(bf16x8, dsf[hh]), acc[db]);
-        }
-      }
-    }
+    const FLUX_LDS char* kl = decltype(BUF)::value ? sm1 : sm0;
+    const FLUX_LDS char* vl = kl + C::TILEB;
+    tile_pass<D, KIND_DQ, decltype(MASK)::value>(kl, vl, kl, nullptr, nullptr, lse, dr, N - k0, qf, of, off, g, acc);
   };
 
   // Tiles alternate between the two LDS buffers; the next tile's loads are
@@ -277,10 +332,10 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   // stay in place; the last one or two tiles (one of them partial) follow.
   const int n_tiles = (N + C::T - 1) / C::T;
   const int n_full = N / C::T;  // tiles without keys past N
-  FLUX_LDS char* const k0s = (FLUX_LDS char*)ksm;
-  FLUX_LDS char* const k1s = (FLUX_LDS char*)ksm + C::TILEB;
-  FLUX_LDS char* const v0s = (FLUX_LDS char*)vsm;
-  FLUX_LDS char* const v1s = (FLUX_LDS char*)vsm + C::TILEB;
+  FLUX_LDS char* const k0s = sm0;
+  FLUX_LDS char* const k1s = sm1;
+  FLUX_LDS char* const v0s = sm0 + C::TILEB;
+  FLUX_LDS char* const v1s = sm1 + C::TILEB;
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   dma_wait();
@@ -344,16 +399,12 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 // their dO and Q~ rows are zero, so they add nothing.  Keys past N only touch
 // their own (unstored) accumulator columns.
 template <int D, bool DK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bwd_dkv_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_dkv(const BwdArgs& a, int blk, FLUX_LDS char* sm0, FLUX_LDS char* sm1) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) char qsm[2 * C::TILEB];  // Q~ tiles (rotated)
-  __shared__ __attribute__((aligned(16))) char osm[2 * C::TILEB];  // dO tiles
-  __shared__ __attribute__((aligned(16))) float lse_s[2 * C::T];   // natural-log lse of the tile's queries
-  __shared__ __attribute__((aligned(16))) float dr_s[2 * C::T];    // Dr of the tile's queries (dK)
+  // buffer b: Q~ tile (rotated) at smb, dO tile at + TILEB, natural-log lse of
+  // the tile's queries at + 2 TILEB, their Dr (dK) after that
   const int N = a.n_tokens, H = a.heads;
   const int k_tiles = (N + C::ROWS - 1) / C::ROWS;
-  const int blk = xcd_tile_order(blockIdx.x, gridDim.x);
   const int kt = blk % k_tiles, bh = blk / k_tiles;
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -371,10 +422,10 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   const TileDma<D> dma(tid, (uint32_t)(ts * 2));
   const uint32_t tile_bytes = (uint32_t)(C::T * ts * 2);
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  FLUX_LDS char* const qs[2] = {(FLUX_LDS char*)qsm, (FLUX_LDS char*)qsm + C::TILEB};
-  FLUX_LDS char* const os[2] = {(FLUX_LDS char*)osm, (FLUX_LDS char*)osm + C::TILEB};
-  FLUX_LDS float* const ls[2] = {(FLUX_LDS float*)lse_s, (FLUX_LDS float*)lse_s + C::T};
-  FLUX_LDS float* const dss[2] = {(FLUX_LDS float*)dr_s, (FLUX_LDS float*)dr_s + C::T};
+  FLUX_LDS char* const qs[2] = {sm0, sm1};
+  FLUX_LDS char* const os[2] = {sm0 + C::TILEB, sm1 + C::TILEB};
+  FLUX_LDS float* const ls[2] = {(FLUX_LDS float*)(sm0 + 2 * C::TILEB), (FLUX_LDS float*)(sm1 + 2 * C::TILEB)};
+  FLUX_LDS float* const dss[2] = {ls[0] + C::T, ls[1] + C::T};
   // tile qt into buffer bf: Q~ and dO rows, lse (wave 0) and Dr (wave 1, dK)
   auto issue = [&](int bf, int qt) {
     dma.issue(qres, qs[bf], (uint32_t)qt * tile_bytes);
@@ -414,60 +465,8 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
 
   auto tile = [&](auto BUF) {
     constexpr int bf = decltype(BUF)::value;
-    const FLUX_LDS char* ql = qs[bf];
-    const FLUX_LDS char* ol = os[bf];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t) {
-        const bf16x8 qfr = __builtin_bit_cast(bf16x8, lds_read_b128(ql + 32 * qb * C::ROWB + off.row[t]));
-        s = mfma_bf16(qfr, kf[t], s);
-        if constexpr (DK) {
-          const bf16x8 ofr = __builtin_bit_cast(bf16x8, lds_read_b128(ol + 32 * qb * C::ROWB + off.row[t]));
-          dp = mfma_bf16(ofr, vf[t], dp);
-        }
-      }
-      // element e: query 32 qb + 16 (e / 8) + 8 g + e % 8 of the tile, this lane's key
-      u32x4 bfr[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int q8 = 32 * qb + 16 * hh + 8 * g;
-        const f32x4 l0 = lds_read_f32x4(ls[bf] + q8), l1 = lds_read_f32x4(ls[bf] + q8 + 4);
-        const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-        float rv[8] = {};
-        if constexpr (DK) {
-          const f32x4 r0 = lds_read_f32x4(dss[bf] + q8), r1 = lds_read_f32x4(dss[bf] + q8 + 4);
-          const float t8[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) rv[i] = t8[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int e = 8 * hh + 2 * i + u;
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(lv[2 * i + u], -1.4426950408889634f, s[e]));
-            v2[u] = DK ? p * (dp[e] - rv[2 * i + u]) : p;
-          }
-          bfr[hh][i] = pack_bf16(v2[0], v2[1]);
-        }
-      }
-      // dV^T += dO^T P  or  dK~^T += Q~^T dS
-      const FLUX_LDS char* al = DK ? ql : ol;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = (32 * qb + 16 * hh) * C::ROWB;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const u32x2 lo = lds_read_tr16(al + r0 + off.tr[db][0]);
-          const u32x2 hi = lds_read_tr16(al + r0 + off.tr[db][1]);
-          const u32x4 aa = {lo[0], lo[1], hi[0], hi[1]};
-          acc[db] = mfma_bf16(__builtin_bit_cast(bf16x8, aa), __builtin_bit_cast(bf16x8, bfr[hh]), acc[db]);
-        }
-      }
-    }
+    tile_pass<D, DK ? KIND_DK : KIND_DV, false>(qs[bf], os[bf], DK ? qs[bf] : os[bf], ls[bf], dss[bf], 0.f, 0.f, 0,
+                                                kf, vf, off, g, acc);
   };
 
   // double-buffered query tiles, as in the dq kernel (no partial-tile case:
@@ -516,27 +515,46 @@ void attn_bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
-// Explicit instantiations: without them hipcc does not emit the host launch
-// stubs of some of these kernels when they are launched from the template below.
+// All three gradients in one launch: workgroups [0, G) compute dK, [G, 2G)
+// dq and [2G, 3G) dV for the G = B H ceil(N / 128) row tiles.  The dispatcher
+// hands out workgroups in index order, so the shorter dV workgroups (two of
+// the products instead of three) fill the last round instead of leaving
+// each gradient's partial last round idle.  One LDS block serves whichever
+// body runs.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  // the two tile buffers are separate LDS objects, so that reads of one are
+  // known not to alias the loads in flight into the other
+  __shared__ __attribute__((aligned(16))) char smem0[2 * C::TILEB + 2 * C::T * (int)sizeof(float)];
+  __shared__ __attribute__((aligned(16))) char smem1[2 * C::TILEB + 2 * C::T * (int)sizeof(float)];
+  FLUX_LDS char* const s0 = (FLUX_LDS char*)smem0;
+  FLUX_LDS char* const s1 = (FLUX_LDS char*)smem1;
+  const int G = gridDim.x / 3;
+  const int seg = blockIdx.x / G, i = blockIdx.x - seg * G;
+  const int blk = xcd_tile_order(i, G);
+  if (seg == 0)
+    bwd_dkv<D, true>(a, blk, s0, s1);
+  else if (seg == 1)
+    bwd_dq<D>(a, blk, s0, s1);
+  else
+    bwd_dkv<D, false>(a, blk, s0, s1);
+}
+
+// Explicit instantiations: without them hipcc does not always emit the host
+// launch stubs of kernels launched from the template below.
 template __global__ void attn_bwd_prep_kernel<128>(BwdArgs);
 template __global__ void attn_bwd_prep_kernel<64>(BwdArgs);
-template __global__ void attn_bwd_dq_kernel<128>(BwdArgs);
-template __global__ void attn_bwd_dq_kernel<64>(BwdArgs);
-template __global__ void attn_bwd_dkv_kernel<128, true>(BwdArgs);
-template __global__ void attn_bwd_dkv_kernel<128, false>(BwdArgs);
-template __global__ void attn_bwd_dkv_kernel<64, true>(BwdArgs);
-template __global__ void attn_bwd_dkv_kernel<64, false>(BwdArgs);
+template __global__ void attn_bwd_kernel<128>(BwdArgs);
+template __global__ void attn_bwd_kernel<64>(BwdArgs);
 
 template <int D>
 static void launch_bwd_kernels(const BwdArgs& a, hipStream_t stream) {
   const long long chunks = (long long)a.batch * a.n_tokens * a.heads * (D / 8);
   const int tiles = a.batch * a.heads * ((a.n_tokens + 127) / 128);
   hipLaunchKernelGGL(attn_bwd_prep_kernel<D>, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a);
-  void (*const dk_kernel)(BwdArgs) = attn_bwd_dkv_kernel<D, true>;
-  void (*const dv_kernel)(BwdArgs) = attn_bwd_dkv_kernel<D, false>;
-  hipLaunchKernelGGL(dk_kernel, dim3(tiles), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(dv_kernel, dim3(tiles), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(tiles), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_kernel<D>, dim3(3 * tiles), dim3(256), 0, stream, a);
 }
 
 hipError_t launch_attn_bwd(const BwdArgs& a, int head_dim, hipStream_t stream) {
