@@ -53,6 +53,7 @@ CASES = [
     ("bw_b2_n257", 2, 2, 128, [S("text", 1), S("image", 16, 16)], 1.0),
     ("bw_d64_n200", 1, 2, 64, [S("text", 8), S("image", 12, 16)], 1.0),
     ("bw_n1", 1, 2, 128, [S("text", 1)], 1.0),
+    ("bw_sigma2_n600", 1, 2, 128, [S("text", 88), S("image", 16, 32)], 2.0),
 ]
 
 

@@ -127,6 +127,22 @@ def test_mutations_are_caught():
         assert not np.allclose(bad[1], ref[1], atol=1e-6)
     finally:
         ob.rope_transpose = orig_rt
+    # mistakes planted in copies of the gradient function's source
+    import inspect
+    src = inspect.getsource(ob.attention_backward)
+    plants = [
+        ("ds = p * (dp - dr)", "ds = p * dp", (0, 1)),                    # dropped Dr term
+        ("dqr[b, :, h] = scale * (ds @ kr[b, :, h])", "dqr[b, :, h] = ds @ kr[b, :, h]", (0,)),  # lost scale
+        ("dv[b, :, h] = p.T @ do", "dv[b, :, h] = p @ do", (2,)),          # transposed P
+        ("dp = do @ v[b, :, h].T", "dp = do @ v[b, :, h].T * scale", (0, 1)),  # spurious factor
+    ]
+    for old, new, hit in plants:
+        assert old in src
+        ns = dict(vars(ob))
+        exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+        bad = ns["attention_backward"](q, k, v, pos, AXES, do)
+        for i in hit:
+            assert not np.allclose(bad[i], ref[i], atol=1e-6), (old, new, i)
     good = ob.attention_backward(q, k, v, pos, AXES, do)
     for g, r in zip(good, ref):
         np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12)
