@@ -101,22 +101,6 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   const uint16_t* vbase = a.v + bat + (size_t)h * D;
   const float c = a.c;
 
-  // ---- Q fragments (B operand of S^T = K Q^T), rotated, held in registers.
-  const int qrow = qt * C::BM + wave * 32 + l32;
-  bf16x8 qf[C::KSTEPS];
-#pragma unroll
-  for (int t = 0; t < C::KSTEPS; ++t) {
-    const int d0 = 16 * t + 8 * g;
-    u32x4 x = {0, 0, 0, 0};
-    f32x4 cs01 = {1.f, 0.f, 1.f, 0.f}, cs23 = {1.f, 0.f, 1.f, 0.f};
-    if (qrow < N) {
-      x = global_load_b128(qbase + (size_t)qrow * tok_stride + d0);
-      const f32x4* rp = (const f32x4*)(a.rope + (size_t)qrow * (D / 2) + d0 / 2);
-      cs01 = rp[0];
-      cs23 = rp[1];
-    }
-    qf[t] = __builtin_bit_cast(bf16x8, rope_chunk_scaled(x, cs01, cs23, c));
-  }
   // Running max folded into the score MFMA: an extra k-step multiplies a
   // column of ones in K by -m in Q, so the accumulator holds c*s - m and
   // p = exp2(acc).  m is kept bf16-representable, so this is exact.  Lanes of
@@ -177,6 +161,53 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int p = 0; p < C::NPASS; ++p) lds_write_b128(vl + v_off<D>(st_row0 + p * C::RPP, st_chunk), vraw[p]);
   };
+
+  // ---- Q fragments (B operand of S^T = K Q^T), rotated, held in registers.
+  // The Q tile is staged like a K tile: coalesced loads of whole rows (16
+  // threads per row) and their angles, rotation, LDS (rows 0-127 in the K
+  // buffers, 128-255 in the V buffers, K row layout), then each lane reads its
+  // fragments.  Loading the fragments directly would touch 32 rows per
+  // instruction and keep the workgroup's memory pipeline busy ~4x longer.
+  // The first K/V tile's loads are issued behind the Q loads.  Rows at or past
+  // N read as zero (buffer range check) and rotate to zero.
+  const int qrow = qt * C::BM + wave * 32 + l32;
+  bf16x8 qf[C::KSTEPS];
+  {
+    constexpr int QCH = C::BM * C::CPR / C::NT;  // chunks per thread
+    static_assert(QCH * C::NT == C::BM * C::CPR && (QCH / 2) * C::RPP == C::BM / 2, "Q staging split");
+    static_assert((C::BM / 2) * (2 * D + 16) <= 2 * C::KTILEB && (C::BM / 2) * (2 * D + 16) <= 2 * C::VTILEB,
+                  "Q staging fits the K and V buffers");
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (size_t)qt * C::BM * tok_stride, tile_bytes(qt * C::BM));
+    const __amdgpu_buffer_rsrc_t rqa =
+        make_rsrc(a.rope + (size_t)qt * C::BM * (D / 2), (uint32_t)((N - qt * C::BM) * (D / 2) * 8));
+    u32x4 qraw[QCH];
+    f32x4 qcs[QCH][2];
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int r = st_row0 + i * C::RPP;
+      qraw[i] = buffer_load_b128(rq, (uint32_t)(r * tok_stride * 2 + st_chunk * 16));
+      qcs[i][0] = __builtin_bit_cast(f32x4, buffer_load_b128(rqa, (uint32_t)(r * (D / 2) * 8 + st_chunk * 32)));
+      qcs[i][1] = __builtin_bit_cast(f32x4, buffer_load_b128(rqa, (uint32_t)(r * (D / 2) * 8 + st_chunk * 32 + 16)));
+    }
+    if (kv0 < kv1) {
+      load_k(kvt(kv0) * C::BN);
+      load_v(kvt(kv0) * C::BN);
+    }
+    auto qrow_lds = [&](int r) -> FLUX_LDS char* {
+      return r < C::BM / 2 ? (FLUX_LDS char*)&ksm[0][0] + k_off<D>(r, 0)
+                           : (FLUX_LDS char*)&vsm[0][0] + k_off<D>(r - C::BM / 2, 0);
+    };
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int r = st_row0 + i * C::RPP;
+      lds_write_b128(qrow_lds(r) + 16 * st_chunk, rope_chunk_scaled(qraw[i], qcs[i][0], qcs[i][1], c));
+    }
+    __syncthreads();
+    const FLUX_LDS char* ql = qrow_lds(wave * 32 + l32);
+#pragma unroll
+    for (int t = 0; t < C::KSTEPS; ++t) qf[t] = __builtin_bit_cast(bf16x8, lds_read_b128(ql + 16 * (2 * t + g)));
+    __syncthreads();  // the K/V buffers are reused below
+  }
 
   f32x16 o[C::DB];
 #pragma unroll
@@ -278,10 +309,8 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   // K(t) is read in iteration t and V(t) in iteration t+1, so K(t+1) and V(t)
   // are written into the buffers that K(t-1) and V(t-2) held: two buffers each.
   if (kv0 < kv1) {  // (a tile-sparse range may be empty: O = 0)
-  load_k(kvt(kv0) * C::BN);
-  store_k(0);
+  store_k(0);  // K and V of the first tile were loaded with Q
   load_k(kvt(kv0 + 1) * C::BN);
-  load_v(kvt(kv0) * C::BN);
   __syncthreads();
 
   u32x4 pp[4];  // P(t-1): fragments (block 0, keys 0-15), (0, 16-31), (1, 0-15), (1, 16-31)
