@@ -58,22 +58,29 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char ksm[2][C::KTILEB];
   __shared__ __attribute__((aligned(16))) char vsm[2][C::VTILEB];
 
-  const int N = a.n_tokens, H = a.heads;
-  const int n_tiles = (N + C::BN - 1) / C::BN;
-  int tile, slot = -1, piece = 0;
+  const int H = a.heads;
+  int tile_g, slot = -1, piece = 0;  // tile in the launch's order
   if ((int)blockIdx.x < a.whole) {
-    tile = xcd_tile_order(blockIdx.x, a.whole);
+    tile_g = xcd_tile_order(blockIdx.x, a.whole);
   } else {
     slot = blockIdx.x - a.whole;
-    tile = a.whole + slot / a.split;
+    tile_g = a.whole + slot / a.split;
     piece = slot % a.split;
   }
+  // The token range this tile belongs to: N tokens from token tok0.
+  int rg = 0;
+  while (rg + 1 < a.nranges && tile_g >= a.rng_tile0[rg + 1]) ++rg;
+  const int N = a.rng_len[rg], tok0 = a.rng_tok0[rg];
+  const int tile = tile_g - a.rng_tile0[rg];
+  const int q_tiles = (N + C::BM - 1) / C::BM;
+  const int n_tiles = (N + C::BN - 1) / C::BN;
+  const float2* const rope = a.rope + (size_t)tok0 * (D / 2);
   // The 64-key tiles this query tile attends to, by position p: all of them
   // (p itself), or in a tile-sparse launch the kept list.  A split piece runs
   // positions [kv0, kv1).  Positions past the range map to a tile past N,
   // whose loads read zeros.
-  const int* kvlist = SPARSE ? a.kv_list + (size_t)tile * a.list_stride : nullptr;
-  const int cnt = SPARSE ? a.kv_count[tile] : n_tiles;
+  const int* kvlist = SPARSE ? a.kv_list + (size_t)tile_g * a.list_stride : nullptr;
+  const int cnt = SPARSE ? a.kv_count[tile_g] : n_tiles;
   int kv0 = 0, kv1 = cnt;
   if (slot >= 0) {
     kv0 = piece * cnt / a.split;
@@ -89,13 +96,13 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   int kv_roll[3] = {0, 0, 0};
   uint32_t kv_ahead = 0;  // list entry of position t+3, loaded during iteration t
   const __amdgpu_buffer_rsrc_t rlist = make_rsrc(kvlist, SPARSE ? (uint32_t)kv1 * 4u : 0u);
-  const int qt = tile % a.q_tiles;
-  const int bh = tile / a.q_tiles;
+  const int qt = tile % q_tiles;
+  const int bh = tile / q_tiles;
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const size_t tok_stride = (size_t)H * D;  // elements between consecutive tokens
-  const size_t bat = (size_t)b * a.batch_tokens * tok_stride;
+  const size_t bat = ((size_t)b * a.batch_tokens + tok0) * tok_stride;  // this batch entry's range
   const uint16_t* qbase = a.q + bat + (size_t)h * D;
   const uint16_t* kbase = a.k + bat + (size_t)h * D;
   const uint16_t* vbase = a.v + bat + (size_t)h * D;
@@ -137,7 +144,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     const int rows = N - kt0;
     const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 8) : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, tile_bytes(kt0));
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rope + (size_t)kt0 * (D / 2), rp_bytes);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rope + (size_t)kt0 * (D / 2), rp_bytes);
 #pragma unroll
     for (int p = 0; p < C::NPASS; ++p) {
       kraw[p] = buffer_load_b128(rk, kv_off[p]);
@@ -179,7 +186,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
                   "Q staging fits the K and V buffers");
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (size_t)qt * C::BM * tok_stride, tile_bytes(qt * C::BM));
     const __amdgpu_buffer_rsrc_t rqa =
-        make_rsrc(a.rope + (size_t)qt * C::BM * (D / 2), (uint32_t)((N - qt * C::BM) * (D / 2) * 8));
+        make_rsrc(rope + (size_t)qt * C::BM * (D / 2), (uint32_t)((N - qt * C::BM) * (D / 2) * 8));
     u32x4 qraw[QCH];
     f32x4 qcs[QCH][2];
 #pragma unroll
@@ -542,11 +549,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int st = idx / per_tile;
   const int rem = idx - st * per_tile;
   const int r = rem / (D / 8), d0 = (rem % (D / 8)) * 8;
-  const int tile = a.whole + st;
-  const int qt = tile % a.q_tiles, bh = tile / a.q_tiles;
+  const int tile_g = a.whole + st;
+  int rg = 0;
+  while (rg + 1 < a.nranges && tile_g >= a.rng_tile0[rg + 1]) ++rg;
+  const int N = a.rng_len[rg], tok0 = a.rng_tok0[rg];
+  const int tile = tile_g - a.rng_tile0[rg];
+  const int q_tiles = (N + 255) / 256;
+  const int qt = tile % q_tiles, bh = tile / q_tiles;
   const int h = bh % a.heads, b = bh / a.heads;
   const int row = qt * 256 + r;
-  if (row >= a.n_tokens) return;
+  if (row >= N) return;
   const int slot0 = st * a.split;
   float m = -INFINITY;
   for (int i = 0; i < a.split; ++i) m = fmaxf(m, a.part_ml[(size_t)(slot0 + i) * 256 + r].x);
@@ -562,17 +574,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;  // 0: no kept keys (tile-sparse)
   if (a.lse != nullptr && d0 == 0)
-    a.lse[((size_t)b * a.heads + h) * a.n_tokens + row] = (m + __builtin_log2f(l)) * 0.6931471805599453f;
+    a.lse[((size_t)b * a.heads + h) * N + row] = (m + __builtin_log2f(l)) * 0.6931471805599453f;
   u32x4 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
   const size_t tok_stride = (size_t)a.heads * D;
-  *(u32x4*)(a.o + (size_t)b * a.batch_tokens * tok_stride + (size_t)row * tok_stride + (size_t)h * D + d0) = out;
+  *(u32x4*)(a.o + ((size_t)b * a.batch_tokens + tok0 + row) * tok_stride + (size_t)h * D + d0) = out;
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream) {
   AttnArgs args = a;
-  args.q_tiles = (a.n_tokens + 255) / 256;
   args.whole = sch.whole_tiles;
   args.split = sch.split;
   const bool sparse = a.kv_list != nullptr;
@@ -592,7 +603,6 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch
 hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream) {
   if (sch.split_tiles == 0) return hipSuccess;
   AttnArgs args = a;
-  args.q_tiles = (a.n_tokens + 255) / 256;
   args.whole = sch.whole_tiles;
   args.split = sch.split;
   const int threads = sch.split_tiles * 256 * (head_dim / 8);

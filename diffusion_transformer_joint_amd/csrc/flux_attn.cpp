@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <mutex>
@@ -305,6 +306,21 @@ int flux_attn_get_config(const flux_attn_plan* plan, flux_attn_config* cfg) {
 
 namespace {
 
+// Fills the range table of a bf16 launch with lens[0..n) (token offsets
+// tok0s) and returns the launch's tile count.
+int set_ranges(flux::AttnArgs& a, const int* tok0s, const int* lens, int n, int batch, int heads) {
+  a.nranges = n;
+  int tiles = 0;
+  for (int r = 0; r < n; ++r) {
+    a.rng_tok0[r] = tok0s[r];
+    a.rng_len[r] = lens[r];
+    a.rng_tile0[r] = tiles;
+    tiles += batch * heads * ((lens[r] + 255) / 256);
+  }
+  a.rng_tile0[n] = tiles;
+  return tiles;
+}
+
 int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void* v, const float* qkv_scale,
                  const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
                  int32_t mode, float* lse, void* hip_stream) {
@@ -326,30 +342,49 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
   const float scale = c.softmax_scale > 0.0f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
   const float log2e = 1.4426950408889634f;
   // Token ranges attended over: the whole sequence (joint), or each non-empty
-  // segment on its own (segment-local).  One attention launch (+ merge) per
-  // range; the ranges run one after another on the stream and share the
-  // plan's partial-state workspace.
+  // segment on its own (segment-local).  bf16: one attention launch (+ merge)
+  // covers up to kMaxRanges ranges, longest first, so that short segments fill
+  // the last round of the long ones; e4m3: one launch per range.  Launches run
+  // one after another on the stream and share the plan's partial-state
+  // workspace.
   const bool joint = mode == FLUX_ATTN_JOINT;
-  const int n_ranges = joint ? 1 : num_segments;
-  int last = 0;  // last non-empty range
-  for (int r = 0; r < n_ranges; ++r)
-    if (joint || segment_tokens[r] > 0) last = r;
+  std::vector<int> tok0s, lens;
+  {
+    int off = 0;
+    for (int r = 0; r < (joint ? 1 : num_segments); ++r) {
+      const int len = joint ? n : segment_tokens[r];
+      if (len > 0) {
+        tok0s.push_back(off);
+        lens.push_back(len);
+      }
+      off += len;
+    }
+  }
+  const bool fp8 = c.dtype == FLUX_ATTN_FP8_E4M3;
+  std::vector<int> order(lens.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+  if (!fp8) std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return lens[x] > lens[y]; });
+  const int per_launch = fp8 ? 1 : flux::AttnArgs::kMaxRanges;
+  const int n_launch = ((int)order.size() + per_launch - 1) / per_launch;
   const bool timed = plan->timing_used < (int)plan->ev_start.size();
   if (timed) {
     e = hipEventRecord(plan->ev_start[plan->timing_used], stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   const size_t tok = (size_t)c.num_heads * c.head_dim;  // elements per token
-  size_t off = 0;
-  for (int r = 0; r < n_ranges; off += joint ? 0 : (size_t)segment_tokens[r], ++r) {
-    const int len = joint ? n : segment_tokens[r];
-    if (len == 0) continue;
-    const int tiles = c.batch * c.num_heads * ((len + 255) / 256);
-    const flux::Schedule sch = flux::plan_schedule(tiles, (len + 63) / 64, plan->num_cus, plan->max_pieces, c.head_dim);
+  for (int li = 0; li < n_launch; ++li) {
+    const int r0 = li * per_launch, r1 = std::min((int)order.size(), r0 + per_launch);
+    int gt[flux::AttnArgs::kMaxRanges], gl[flux::AttnArgs::kMaxRanges];
+    int max_len = 0;
+    for (int r = r0; r < r1; ++r) {
+      gt[r - r0] = tok0s[order[r]];
+      gl[r - r0] = lens[order[r]];
+      max_len = std::max(max_len, gl[r - r0]);
+    }
     flux::AttnArgs a{};
-    a.o = static_cast<uint16_t*>(out) + off * tok;
-    a.rope = plan->rope_table + off * (c.head_dim / 2);
-    a.n_tokens = len;
+    const int tiles = set_ranges(a, gt, gl, r1 - r0, c.batch, c.num_heads);
+    const flux::Schedule sch = flux::plan_schedule(tiles, (max_len + 63) / 64, plan->num_cus, plan->max_pieces,
+                                                   c.head_dim);
     a.batch_tokens = n;
     a.heads = c.num_heads;
     a.batch = c.batch;
@@ -357,15 +392,16 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
     a.part_o = plan->part_o;
     a.part_ml = plan->part_ml;
     a.lse = lse;
-    if (c.dtype == FLUX_ATTN_FP8_E4M3) {
+    if (fp8) {
+      const size_t off = (size_t)gt[0];
       flux::Fp8Args f{};
       f.q = static_cast<const uint8_t*>(q) + off * tok;
       f.k = static_cast<const uint8_t*>(k) + off * tok;
       f.v = static_cast<const uint8_t*>(v) + off * tok;
       f.scales = qkv_scale;
-      f.o = a.o;
-      f.rope = a.rope;
-      f.n_tokens = len;
+      f.o = static_cast<uint16_t*>(out) + off * tok;
+      f.rope = plan->rope_table + off * (c.head_dim / 2);
+      f.n_tokens = gl[0];
       f.batch_tokens = n;
       f.heads = c.num_heads;
       f.batch = c.batch;
@@ -373,16 +409,23 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
       f.part_o = a.part_o;
       f.part_ml = a.part_ml;
       e = flux::launch_attn_fp8(f, c.head_dim, sch, stream);
+      // the e4m3 merge reads the same fields through AttnArgs: one range at
+      // offset 0 of the shifted pointers
+      a.o = f.o;
+      gt[0] = 0;
+      set_ranges(a, gt, gl, 1, c.batch, c.num_heads);
     } else {
-      a.q = static_cast<const uint16_t*>(q) + off * tok;
-      a.k = static_cast<const uint16_t*>(k) + off * tok;
-      a.v = static_cast<const uint16_t*>(v) + off * tok;
+      a.q = static_cast<const uint16_t*>(q);
+      a.k = static_cast<const uint16_t*>(k);
+      a.v = static_cast<const uint16_t*>(v);
+      a.o = static_cast<uint16_t*>(out);
+      a.rope = plan->rope_table;
       e = flux::launch_attn_bf16(a, c.head_dim, sch, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     // The joint call's timing pair brackets its attention kernel alone; in
-    // segment-local mode it spans all ranges (merges between them included).
-    if (timed && r == last) {
+    // segment-local mode it spans all launches (merges between them included).
+    if (timed && li == n_launch - 1) {
       e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
       if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
       ++plan->timing_used;
@@ -563,7 +606,10 @@ int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k,
   a.v = static_cast<const uint16_t*>(v);
   a.o = static_cast<uint16_t*>(out);
   a.rope = plan->rope_table;
-  a.n_tokens = n;
+  {
+    const int t0 = 0;
+    set_ranges(a, &t0, &n, 1, c.batch, c.num_heads);
+  }
   a.batch_tokens = n;
   a.heads = c.num_heads;
   a.batch = c.batch;

@@ -11,11 +11,9 @@ struct AttnArgs {
   const uint16_t* v;
   uint16_t* o;            // [B][N][H][D] bf16 bits
   const float2* rope;     // [N][D/2] (cos, sin)
-  int n_tokens;           // tokens attended over (one segment in segment-local mode)
   int batch_tokens;       // tokens between consecutive batch entries of q, k, v, o
   int heads;
   int batch;
-  int q_tiles;            // filled by the launcher
   float c;                // softmax scale * log2(e)
   // Work split (see Schedule): blocks [0, whole) run whole query tiles; the
   // other blocks run one of `split` K/V ranges of the remaining tiles and write
@@ -29,8 +27,19 @@ struct AttnArgs {
   const int* kv_list;
   const int* kv_count;
   int list_stride;
-  // Optional: natural-log log-sum-exp of each row of scale * S, [B][H][N].
+  // Optional: natural-log log-sum-exp of each row of scale * S, [B][H][N]
+  // (single-range launches).
   float* lse;
+  // Token ranges of the launch (bf16 kernel): range r attends over tokens
+  // [rng_tok0[r], rng_tok0[r] + rng_len[r]) of the sequence (q, k, v, o and
+  // rope point at token 0) and owns the launch's tiles [rng_tile0[r],
+  // rng_tile0[r + 1]).  Joint attention is one range; segment-local mode puts
+  // up to kMaxRanges segments into one launch.
+  static constexpr int kMaxRanges = 16;
+  int nranges;
+  int rng_tok0[kMaxRanges];
+  int rng_len[kMaxRanges];
+  int rng_tile0[kMaxRanges + 1];
 };
 
 // How one launch covers T query tiles of 256 rows with K/V ranges of n_kv
