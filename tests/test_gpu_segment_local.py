@@ -77,3 +77,19 @@ def test_fp8_segment_local():
     inp = I.make_inputs(custom("seg_fp8", 3, 128, [S("text", 60), S("image", 16, 16)], fp8=True))
     got = out_fp64(run_hip(inp, mode="segment_local"))
     assert_close(got, ref_full(inp, mode="segment_local"), FP8_TOL, "fp8 segment-local")
+
+
+def test_segment_local_many_segments():
+    # 18 non-empty segments (two launches of at most 16 token ranges each),
+    # ragged lengths from 1 to 300 tokens and two empty segments.
+    from diffusion_transformer_joint_amd.flux_attn import Plan
+    lens = [300, 5, 0, 17, 64, 1, 129, 33, 0, 256, 7, 90, 2, 45, 3, 12, 70, 200, 9, 31]
+    segs = [S("text", n) for n in lens]
+    inp = I.make_inputs(custom("seg_many", 2, 128, segs, sigma=1.0))
+    w = inp.workload
+    plan = Plan(w.batch, w.heads, w.head_dim, w.tokens, max_segments=len(lens))
+    try:
+        got = out_fp64(run_hip(inp, plan=plan, mode="segment_local"))
+    finally:
+        plan.close()
+    assert_close(got, ref_full(inp, mode="segment_local"), BF16_TOL, "seg_many")
