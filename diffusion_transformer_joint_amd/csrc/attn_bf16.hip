@@ -61,10 +61,11 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   const int H = a.heads;
   int tile_g, slot = -1, piece = 0;  // tile in the launch's order
   if ((int)blockIdx.x < a.whole) {
-    tile_g = xcd_tile_order(blockIdx.x, a.whole);
+    tile_g = a.tile_order != nullptr ? a.tile_order[blockIdx.x] : xcd_tile_order(blockIdx.x, a.whole);
   } else {
     slot = blockIdx.x - a.whole;
     tile_g = a.whole + slot / a.split;
+    if (a.tile_order != nullptr) tile_g = a.tile_order[tile_g];
     piece = slot % a.split;
   }
   // The token range this tile belongs to: N tokens from token tok0.
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int st = idx / per_tile;
   const int rem = idx - st * per_tile;
   const int r = rem / (D / 8), d0 = (rem % (D / 8)) * 8;
-  const int tile_g = a.whole + st;
+  const int tile_g = a.tile_order != nullptr ? a.tile_order[a.whole + st] : a.whole + st;
   int rg = 0;
   while (rg + 1 < a.nranges && tile_g >= a.rng_tile0[rg + 1]) ++rg;
   const int N = a.rng_len[rg], tok0 = a.rng_tok0[rg];

@@ -104,6 +104,36 @@ __global__ __launch_bounds__(256) void mask_to_list_kernel(const uint8_t* __rest
   if (lane == 0) count[row] = n;
 }
 
+// Dispatch order of a tile-sparse launch: query tiles by kept count,
+// longest first (ties by index, so the order and with it the split of the
+// last round are deterministic).  One workgroup sorts the keys
+// (KT - count) << IB | index with a bitonic network in LDS.
+__global__ __launch_bounds__(1024) void tile_order_kernel(const int* __restrict__ count, int* __restrict__ order,
+                                                          int rows, int KT, int P, int IB) {
+  extern __shared__ uint32_t key[];  // [P], P = power of two >= rows
+  for (int i = threadIdx.x; i < P; i += 1024)
+    key[i] = i < rows ? ((uint32_t)(KT - count[i]) << IB) | (uint32_t)i : 0xffffffffu;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < P; i += 1024) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t a = key[i], b = key[l];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) {
+            key[i] = b;
+            key[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < rows; i += 1024) order[i] = (int)(key[i] & ((1u << IB) - 1u));
+}
+
+
 hipError_t launch_tile_means(const uint16_t* x, const float2* rope, float* out, int n_tokens, int batch_tokens,
                              int heads, int batch, int head_dim, int tile, hipStream_t stream) {
   const int T = (n_tokens + tile - 1) / tile;
@@ -116,6 +146,16 @@ hipError_t launch_tile_means(const uint16_t* x, const float2* rope, float* out, 
                        heads, tile, T);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_order(const int* count, int* order, int rows, int KT, hipStream_t stream) {
+  int P = 1, IB = 0;
+  while (P < rows) P <<= 1;
+  while ((1 << IB) < P) ++IB;
+  if (P > 32768 || ((uint64_t)KT << IB) >= (1ull << 32)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(1024), (size_t)P * sizeof(uint32_t), stream, count, order, rows,
+                     KT, P, IB);
   return hipGetLastError();
 }
 

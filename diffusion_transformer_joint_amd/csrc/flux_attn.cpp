@@ -68,6 +68,7 @@ struct flux_attn_plan {
   float* kbar = nullptr;         // [B][H][KT][D]
   int* kv_list = nullptr;        // [B*H*QT][KT]
   int* kv_count = nullptr;       // [B*H*QT]
+  int* tile_order = nullptr;     // [B*H*QT] dispatch order of a tile-sparse launch
   float* dr = nullptr;           // backward: rowsum(dO * O), [B][H][N]
   uint16_t* rq = nullptr;        // backward: bf16 R(q), R(k), [B][N][H][D]
   uint16_t* rk = nullptr;
@@ -269,6 +270,7 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     if (e == hipSuccess) e = hipMalloc(&p->kbar, rows * kt * cfg->head_dim * sizeof(float));
     if (e == hipSuccess) e = hipMalloc(&p->kv_list, rows * qt * kt * sizeof(int));
     if (e == hipSuccess) e = hipMalloc(&p->kv_count, rows * qt * sizeof(int));
+    if (e == hipSuccess) e = hipMalloc(&p->tile_order, rows * qt * sizeof(int));
     if (e == hipSuccess) e = hipMalloc(&p->dr, rows * cfg->max_tokens * sizeof(float));
     const size_t elems = rows * cfg->max_tokens * cfg->head_dim;
     if (e == hipSuccess) e = hipMalloc(&p->rq, elems * sizeof(uint16_t));
@@ -283,6 +285,7 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     (void)hipFree(p->kbar);
     (void)hipFree(p->kv_list);
     (void)hipFree(p->kv_count);
+    (void)hipFree(p->tile_order);
     (void)hipFree(p->dr);
     (void)hipFree(p->rq);
     (void)hipFree(p->rk);
@@ -599,6 +602,13 @@ int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k,
   const int rows = c.batch * c.num_heads * QT;
   e = flux::launch_mask_to_list(mask, plan->kv_list, plan->kv_count, rows, KT, KT, stream);
   if (e != hipSuccess) return hip_fail(e, "mask compaction launch");
+  // Longest lists first: tiles run in order of kept count, so that the last
+  // round is made of the shortest ones (and of the split pieces).
+  const bool ordered = rows <= 32768;
+  if (ordered) {
+    e = flux::launch_tile_order(plan->kv_count, plan->tile_order, rows, KT, stream);
+    if (e != hipSuccess) return hip_fail(e, "tile order launch");
+  }
   const flux::Schedule sch = flux::plan_schedule(rows, KT, plan->num_cus, plan->max_pieces, c.head_dim);
   flux::AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -619,6 +629,7 @@ int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k,
   a.kv_list = plan->kv_list;
   a.kv_count = plan->kv_count;
   a.list_stride = KT;
+  a.tile_order = ordered ? plan->tile_order : nullptr;
   const bool timed = plan->timing_used < (int)plan->ev_start.size();
   if (timed) {
     e = hipEventRecord(plan->ev_start[plan->timing_used], stream);
@@ -705,6 +716,7 @@ int flux_attn_destroy(flux_attn_plan* plan) {
   (void)hipFree(plan->kbar);
   (void)hipFree(plan->kv_list);
   (void)hipFree(plan->kv_count);
+  (void)hipFree(plan->tile_order);
   (void)hipFree(plan->dr);
   (void)hipFree(plan->rq);
   (void)hipFree(plan->rk);

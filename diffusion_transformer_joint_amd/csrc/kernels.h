@@ -27,6 +27,9 @@ struct AttnArgs {
   const int* kv_list;
   const int* kv_count;
   int list_stride;
+  // Optional (tile-sparse): dispatch order of the tiles; whole tiles run in
+  // this order and the last ones in it are split.
+  const int* tile_order;
   // Optional: natural-log log-sum-exp of each row of scale * S, [B][H][N]
   // (single-range launches).
   float* lse;
@@ -116,5 +119,8 @@ hipError_t launch_block_select(const float* qbar, const float* kbar, uint8_t* ma
 // Kept key tiles of each mask row (ascending) into list[row * stride + i], count[row].
 hipError_t launch_mask_to_list(const uint8_t* mask, int* list, int* count, int rows, int KT, int stride,
                                hipStream_t stream);
+// Query tiles ordered by kept count, descending (ties by index): order[rows].
+// hipErrorInvalidValue when rows > 32768 (the caller keeps the natural order).
+hipError_t launch_tile_order(const int* count, int* order, int rows, int KT, hipStream_t stream);
 
 }  // namespace flux
