@@ -51,23 +51,16 @@ struct Bf16Cfg {
   static constexpr int VTILEB = BN * (2 * D + 64);  // bytes per V tile in LDS
 };
 
+// One work item: query tile tile_g (in the launch's tile order) over its K/V
+// positions [kvx0, kvx1), or, with kvx0 < 0, over piece `piece` of `a.split`
+// (slot >= 0) or all of them (slot < 0).  slot >= 0: the fp32 partial state
+// goes to workspace slot `slot`; otherwise O is written.
 template <int D, bool SPARSE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_bf16_kernel(AttnArgs a) {
+__device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16Cfg<D>::KTILEB],
+                                         char (&vsm)[2][Bf16Cfg<D>::VTILEB], int tile_g, int slot, int piece,
+                                         int kvx0, int kvx1) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char ksm[2][C::KTILEB];
-  __shared__ __attribute__((aligned(16))) char vsm[2][C::VTILEB];
-
   const int H = a.heads;
-  int tile_g, slot = -1, piece = 0;  // tile in the launch's order
-  if ((int)blockIdx.x < a.whole) {
-    tile_g = a.tile_order != nullptr ? a.tile_order[blockIdx.x] : xcd_tile_order(blockIdx.x, a.whole);
-  } else {
-    slot = blockIdx.x - a.whole;
-    tile_g = a.whole + slot / a.split;
-    if (a.tile_order != nullptr) tile_g = a.tile_order[tile_g];
-    piece = slot % a.split;
-  }
   // The token range this tile belongs to: N tokens from token tok0.
   int rg = 0;
   while (rg + 1 < a.nranges && tile_g >= a.rng_tile0[rg + 1]) ++rg;
@@ -83,7 +76,10 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   const int* kvlist = SPARSE ? a.kv_list + (size_t)tile_g * a.list_stride : nullptr;
   const int cnt = SPARSE ? a.kv_count[tile_g] : n_tiles;
   int kv0 = 0, kv1 = cnt;
-  if (slot >= 0) {
+  if (kvx0 >= 0) {
+    kv0 = kvx0;
+    kv1 = kvx1;
+  } else if (slot >= 0) {
     kv0 = piece * cnt / a.split;
     kv1 = (piece + 1) * cnt / a.split;
   }
@@ -541,6 +537,99 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   }
 }
 
+template <int D, bool SPARSE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_kernel(AttnArgs a) {
+  using C = Bf16Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char ksm[2][C::KTILEB];
+  __shared__ __attribute__((aligned(16))) char vsm[2][C::VTILEB];
+  // Persistent split (sk_nkv > 0, one workgroup per CU): the launch's tiles x
+  // K/V positions, flattened, are cut into gridDim.x equal slices; a slice
+  // runs the pieces of the tiles it covers one after the other.  A piece that
+  // is not a whole tile stores its partial state in slot 2c (the slice's first
+  // tile) or 2c + 1 (its last), and attn_merge_sk_kernel combines them.
+  // Slices of one XCD are adjacent.  Otherwise one work item per workgroup.
+  const bool sk = !SPARSE && a.sk_nkv > 0;
+  const int nkv = sk ? a.sk_nkv : 1;
+  const int cu = sk ? xcd_tile_order(blockIdx.x, gridDim.x) : 0;
+  const long W = sk ? (long)a.sk_tiles * nkv : 0;
+  const long hi = sk ? W * (cu + 1) / gridDim.x : 1;
+  long pos = sk ? W * cu / gridDim.x : 0;
+  const int first = (int)(pos / nkv);
+  while (pos < hi) {
+    int tile_g, slot = -1, piece = 0, k0 = -1, k1 = -1;
+    long next = hi;
+    if (sk) {
+      tile_g = (int)(pos / nkv);
+      next = hi < (long)(tile_g + 1) * nkv ? hi : (long)(tile_g + 1) * nkv;
+      k0 = (int)(pos - (long)tile_g * nkv);
+      k1 = (int)(next - (long)tile_g * nkv);
+      if (k0 != 0 || k1 != nkv) slot = 2 * cu + (tile_g == first ? 0 : 1);
+    } else if ((int)blockIdx.x < a.whole) {
+      tile_g = a.tile_order != nullptr ? a.tile_order[blockIdx.x] : xcd_tile_order(blockIdx.x, a.whole);
+    } else {
+      slot = blockIdx.x - a.whole;
+      tile_g = a.whole + slot / a.split;
+      if (a.tile_order != nullptr) tile_g = a.tile_order[tile_g];
+      piece = slot % a.split;
+    }
+    fwd_tile<D, SPARSE>(a, ksm, vsm, tile_g, slot, piece, k0, k1);
+    pos = next;
+    if (pos < hi) __syncthreads();  // the next piece reuses the LDS buffers
+  }
+}
+
+// Merge of a persistent-split launch: block (c - 1) * 16 + sub, for each
+// slice boundary c in [1, gridDim/16], takes rows 16 sub .. 16 sub + 15 of
+// the tile that the boundary cuts (if it is the first boundary inside it),
+// 16 threads per row, 8 dims each, and combines the partials of the slices
+// that cover the tile.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_sk_kernel(AttnArgs a) {
+  const int ncu = a.sk_cus, nkv = a.sk_nkv;
+  const long W = (long)a.sk_tiles * nkv;
+  const int c = blockIdx.x / 16 + 1, sub = blockIdx.x % 16;
+  const long bc = W * c / ncu;
+  if (bc % nkv == 0) return;  // the boundary falls between tiles
+  const int T = (int)(bc / nkv);
+  const long t_start = (long)T * nkv, t_end = t_start + nkv;
+  if (c > 1 && W * (c - 1) / ncu > t_start) return;  // an earlier boundary cuts T
+  const int r = sub * 16 + (threadIdx.x >> 4), d0 = (threadIdx.x & 15) * 8;
+  const int N = a.rng_len[0];
+  const int q_tiles = (N + 255) / 256;
+  const int qt = T % q_tiles, bh = T / q_tiles;
+  const int h = bh % a.heads, b = bh / a.heads;
+  const int row = qt * 256 + r;
+  if (row >= N) return;
+  // slices c - 1 .. c_last cover T; slice c' keeps T's piece in slot 2c' when
+  // T is its first tile, else 2c' + 1
+  auto slot_of = [&](int cc) { return 2 * cc + ((W * cc / ncu) / nkv == T ? 0 : 1); };
+  float m = -INFINITY;
+  auto empty = [&](int cc) { return W * (cc + 1) / ncu == W * cc / ncu; };
+  for (int cc = c - 1; cc < ncu && W * cc / ncu < t_end; ++cc)
+    if (!empty(cc)) m = fmaxf(m, a.part_ml[(size_t)slot_of(cc) * 256 + r].x);
+  float l = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int cc = c - 1; cc < ncu && W * cc / ncu < t_end; ++cc) {
+    if (empty(cc)) continue;
+    const int sl = slot_of(cc);
+    const float2 ml = a.part_ml[(size_t)sl * 256 + r];
+    const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - m) : 0.f;
+    l += w * ml.y;
+    const float* po = a.part_o + ((size_t)sl * 256 + r) * D + d0;
+    const f32x4 x0 = *(const f32x4*)po, x1 = *(const f32x4*)(po + 4);
+    acc[0] += w * x0[0]; acc[1] += w * x0[1]; acc[2] += w * x0[2]; acc[3] += w * x0[3];
+    acc[4] += w * x1[0]; acc[5] += w * x1[1]; acc[6] += w * x1[2]; acc[7] += w * x1[3];
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  if (a.lse != nullptr && d0 == 0)
+    a.lse[((size_t)b * a.heads + h) * N + row] = (m + __builtin_log2f(l)) * 0.6931471805599453f;
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  const size_t tok_stride = (size_t)a.heads * D;
+  *(u32x4*)(a.o + ((size_t)b * a.batch_tokens + row) * tok_stride + (size_t)h * D + d0) = out;
+}
+
 // One thread per (split tile, row, 8 output dims): combines the `split`
 // partial states of its row exactly and writes bf16.
 template <int D>
@@ -587,6 +676,9 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch
   AttnArgs args = a;
   args.whole = sch.whole_tiles;
   args.split = sch.split;
+  args.sk_nkv = sch.sk_nkv;
+  args.sk_tiles = sch.sk_tiles;
+  args.sk_cus = sch.sk_cus;
   const bool sparse = a.kv_list != nullptr;
   if (head_dim == 128 && !sparse)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), dim3(sch.grid), dim3(Bf16Cfg<128>::NT), 0, stream, args);
@@ -602,6 +694,21 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch
 }
 
 hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream) {
+  if (sch.sk_nkv > 0) {
+    AttnArgs args = a;
+    args.sk_nkv = sch.sk_nkv;
+    args.sk_tiles = sch.sk_tiles;
+    args.sk_cus = sch.sk_cus;
+    const dim3 grid((unsigned)(16 * (sch.sk_cus - 1)));
+    if (sch.sk_cus < 2) return hipSuccess;
+    if (head_dim == 128)
+      hipLaunchKernelGGL(attn_merge_sk_kernel<128>, grid, dim3(256), 0, stream, args);
+    else if (head_dim == 64)
+      hipLaunchKernelGGL(attn_merge_sk_kernel<64>, grid, dim3(256), 0, stream, args);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (sch.split_tiles == 0) return hipSuccess;
   AttnArgs args = a;
   args.whole = sch.whole_tiles;

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <mutex>
 #include <new>
 #include <unordered_set>
@@ -74,6 +75,7 @@ struct flux_attn_plan {
   uint16_t* rk = nullptr;
   int num_cus = 0;
   int max_pieces = 0;
+  int sched_mode = 0;  // FLUX_ATTN_SCHEDULE at creation: 0 by cost, 1 'split', 2 'persistent'
   std::vector<hipEvent_t> ev_start, ev_stop;  // kernel timing pairs
   int timing_used = 0;
 };
@@ -247,6 +249,11 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     delete p;
     return hip_fail(e, "hipDeviceGetAttribute");
   }
+  // Schedule override for tests and measurements (the default is by cost).
+  if (const char* sm = std::getenv("FLUX_ATTN_SCHEDULE")) {
+    if (std::strcmp(sm, "split") == 0) p->sched_mode = 1;
+    if (std::strcmp(sm, "persistent") == 0) p->sched_mode = 2;
+  }
   // Split-K/V partials: at most 4 pieces per compute unit, and no more than
   // the launch can produce at max_tokens.
   {
@@ -386,8 +393,11 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
     }
     flux::AttnArgs a{};
     const int tiles = set_ranges(a, gt, gl, r1 - r0, c.batch, c.num_heads);
-    const flux::Schedule sch = flux::plan_schedule(tiles, (max_len + 63) / 64, plan->num_cus, plan->max_pieces,
-                                                   c.head_dim);
+    const flux::Schedule sch =
+        (!fp8 && r1 - r0 == 1)
+            ? flux::plan_schedule_dense(tiles, (max_len + 63) / 64, plan->num_cus, plan->max_pieces, c.head_dim,
+                                        plan->sched_mode)
+            : flux::plan_schedule(tiles, (max_len + 63) / 64, plan->num_cus, plan->max_pieces, c.head_dim);
     a.batch_tokens = n;
     a.heads = c.num_heads;
     a.batch = c.batch;

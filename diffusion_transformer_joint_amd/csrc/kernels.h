@@ -20,6 +20,7 @@ struct AttnArgs {
   // fp32 partials that attn_merge combines.
   int whole;
   int split;
+  int sk_nkv, sk_tiles, sk_cus;  // persistent split (see Schedule); sk_nkv = 0: off
   float* part_o;          // [slot][256][D] un-normalized O of each partial
   float2* part_ml;        // [slot][256] (running max in the exp2 domain, row sum)
   // Tile-sparse launches only: kept 64-key tiles of each 256-row query tile,
@@ -54,8 +55,16 @@ struct Schedule {
   int split_tiles;
   int split;
   int grid;
+  // Persistent split instead (sk_nkv > 0): grid = sk_cus workgroups, each
+  // runs an equal slice of the sk_tiles x sk_nkv tile positions.
+  int sk_nkv = 0;
+  int sk_tiles = 0;
+  int sk_cus = 0;
 };
 Schedule plan_schedule(int tiles, int kv_tiles, int num_cus, int max_pieces, int head_dim);
+// Dense single-range bf16 launches: plan_schedule's split or the persistent
+// one (mode 0: by cost, 1: never persistent, 2: persistent where possible).
+Schedule plan_schedule_dense(int tiles, int kv_tiles, int num_cus, int max_pieces, int head_dim, int mode);
 
 struct Fp8Args {
   const uint8_t* q;       // [B][N][H][D] e4m3 codes

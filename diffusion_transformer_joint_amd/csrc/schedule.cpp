@@ -43,4 +43,26 @@ Schedule plan_schedule(int tiles, int kv_tiles, int num_cus, int max_pieces, int
   return best;
 }
 
+// Dense single-range launches: the split above, or a persistent split in
+// which each of the C workgroups runs an equal slice of the T x kv_tiles tile
+// positions (partials in at most 2 C slots).  Measured on the 8,704-token
+// call: with T >= C (3 heads x 24 would be 816 tiles) the persistent split
+// loses (-9%): a static slice cannot absorb the +-5% spread of per-CU speed
+// that the hardware's dynamic dispatch of split pieces evens out; with T < C
+// (one GPU's 3-head share: 102 tiles) it wins (+10%) over cutting every tile
+// into 5 pieces and running them in two rounds.  So: persistent when T < C
+// and every slice gets at least two positions (mode 0), always where the
+// workspace allows (mode 2), or never (mode 1).
+Schedule plan_schedule_dense(int tiles, int kv_tiles, int num_cus, int max_pieces, int head_dim, int mode) {
+  const Schedule base = plan_schedule(tiles, kv_tiles, num_cus, max_pieces, head_dim);
+  if (mode == 1 || tiles <= 0 || kv_tiles <= 0 || num_cus < 2 || 2 * num_cus > max_pieces) return base;
+  Schedule s{0, 0, 1, num_cus};
+  s.sk_nkv = kv_tiles;
+  s.sk_tiles = tiles;
+  s.sk_cus = num_cus;
+  if (mode == 2) return s;
+  const long W = (long)tiles * kv_tiles;
+  return (tiles < num_cus && W >= 2L * num_cus) ? s : base;
+}
+
 }  // namespace flux
