@@ -107,16 +107,43 @@ __global__ __launch_bounds__(256) void mask_to_list_kernel(const uint8_t* __rest
 // Dispatch order of a tile-sparse launch: query tiles by kept count,
 // longest first (ties by index, so the order and with it the split of the
 // last round are deterministic).  One workgroup sorts the keys
-// (KT - count) << IB | index with a bitonic network in LDS.
+// (KT - count) << IB | index with a bitonic network.  Up to 1024 rows each
+// thread holds one key in a register: the compare-exchange steps with
+// partners inside the wave (distance < 64) use shuffles, only the longer ones
+// go through LDS with a barrier; larger row counts sort in LDS throughout.
 __global__ __launch_bounds__(1024) void tile_order_kernel(const int* __restrict__ count, int* __restrict__ order,
                                                           int rows, int KT, int P, int IB) {
-  extern __shared__ uint32_t key[];  // [P], P = power of two >= rows
-  for (int i = threadIdx.x; i < P; i += 1024)
-    key[i] = i < rows ? ((uint32_t)(KT - count[i]) << IB) | (uint32_t)i : 0xffffffffu;
+  extern __shared__ uint32_t key[];  // [max(P, 1024)], P = power of two >= rows
+  const int tid = threadIdx.x;
+  auto make_key = [&](int i) -> uint32_t {
+    return i < rows ? ((uint32_t)(KT - count[i]) << IB) | (uint32_t)i : 0xffffffffu;
+  };
+  if (P <= 1024) {
+    uint32_t x = tid < P ? make_key(tid) : 0xffffffffu;
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        uint32_t y;
+        if (j >= 64) {
+          key[tid] = x;
+          __syncthreads();
+          y = key[tid ^ j];
+          __syncthreads();
+        } else {
+          y = (uint32_t)__shfl_xor((int)x, j);
+        }
+        const bool lower = (tid & j) == 0, up = (tid & k) == 0;
+        // the lower element of an ascending pair keeps the smaller key
+        x = (lower == up) ? (x < y ? x : y) : (x < y ? y : x);
+      }
+    }
+    if (tid < rows) order[tid] = (int)(x & ((1u << IB) - 1u));
+    return;
+  }
+  for (int i = tid; i < P; i += 1024) key[i] = make_key(i);
   __syncthreads();
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += 1024) {
+      for (int i = tid; i < P; i += 1024) {
         const int l = i ^ j;
         if (l > i) {
           const uint32_t a = key[i], b = key[l];
@@ -130,9 +157,8 @@ __global__ __launch_bounds__(1024) void tile_order_kernel(const int* __restrict_
       __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < rows; i += 1024) order[i] = (int)(key[i] & ((1u << IB) - 1u));
+  for (int i = tid; i < rows; i += 1024) order[i] = (int)(key[i] & ((1u << IB) - 1u));
 }
-
 
 hipError_t launch_tile_means(const uint16_t* x, const float2* rope, float* out, int n_tokens, int batch_tokens,
                              int heads, int batch, int head_dim, int tile, hipStream_t stream) {
@@ -154,8 +180,9 @@ hipError_t launch_tile_order(const int* count, int* order, int rows, int KT, hip
   while (P < rows) P <<= 1;
   while ((1 << IB) < P) ++IB;
   if (P > 32768 || ((uint64_t)KT << IB) >= (1ull << 32)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(1024), (size_t)P * sizeof(uint32_t), stream, count, order, rows,
-                     KT, P, IB);
+  // the register path stores one key per thread (1024) in its LDS steps
+  const size_t lds = (size_t)(P > 1024 ? P : 1024) * sizeof(uint32_t);
+  hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(1024), lds, stream, count, order, rows, KT, P, IB);
   return hipGetLastError();
 }
 
