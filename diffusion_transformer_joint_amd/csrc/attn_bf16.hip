@@ -568,7 +568,8 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     } else if ((int)blockIdx.x < a.whole) {
       tile_g = a.tile_order != nullptr ? a.tile_order[blockIdx.x] : xcd_tile_order(blockIdx.x, a.whole);
     } else {
-      slot = blockIdx.x - a.whole;
+      // pieces of neighbouring tiles on one XCD, like the whole tiles
+      slot = xcd_tile_order(blockIdx.x - a.whole, gridDim.x - a.whole);
       tile_g = a.whole + slot / a.split;
       if (a.tile_order != nullptr) tile_g = a.tile_order[tile_g];
       piece = slot % a.split;
