@@ -537,44 +537,51 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
   }
 }
 
+// One work item per workgroup: whole tiles first (XCD-contiguous, or in the
+// given order), then the split pieces of the last round.
 template <int D, bool SPARSE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_kernel(AttnArgs a) {
   using C = Bf16Cfg<D>;
   __shared__ __attribute__((aligned(16))) char ksm[2][C::KTILEB];
   __shared__ __attribute__((aligned(16))) char vsm[2][C::VTILEB];
-  // Persistent split (sk_nkv > 0, one workgroup per CU): the launch's tiles x
-  // K/V positions, flattened, are cut into gridDim.x equal slices; a slice
-  // runs the pieces of the tiles it covers one after the other.  A piece that
-  // is not a whole tile stores its partial state in slot 2c (the slice's first
-  // tile) or 2c + 1 (its last), and attn_merge_sk_kernel combines them.
-  // Slices of one XCD are adjacent.  Otherwise one work item per workgroup.
-  const bool sk = !SPARSE && a.sk_nkv > 0;
-  const int nkv = sk ? a.sk_nkv : 1;
-  const int cu = sk ? xcd_tile_order(blockIdx.x, gridDim.x) : 0;
-  const long W = sk ? (long)a.sk_tiles * nkv : 0;
-  const long hi = sk ? W * (cu + 1) / gridDim.x : 1;
-  long pos = sk ? W * cu / gridDim.x : 0;
+  int tile_g, slot = -1, piece = 0;
+  if ((int)blockIdx.x < a.whole) {
+    tile_g = a.tile_order != nullptr ? a.tile_order[blockIdx.x] : xcd_tile_order(blockIdx.x, a.whole);
+  } else {
+    // pieces of neighbouring tiles on one XCD, like the whole tiles
+    slot = xcd_tile_order(blockIdx.x - a.whole, gridDim.x - a.whole);
+    tile_g = a.whole + slot / a.split;
+    if (a.tile_order != nullptr) tile_g = a.tile_order[tile_g];
+    piece = slot % a.split;
+  }
+  fwd_tile<D, SPARSE>(a, ksm, vsm, tile_g, slot, piece, -1, -1);
+}
+
+// Persistent split (one workgroup per CU, dense): the launch's tiles x K/V
+// positions, flattened, are cut into gridDim.x equal slices; a slice runs the
+// pieces of the tiles it covers one after the other.  A piece that is not a
+// whole tile stores its partial state in slot 2c (the slice's first tile) or
+// 2c + 1 (its last), and attn_merge_sk_kernel combines them.  Slices of one
+// XCD are adjacent.
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_persistent_kernel(AttnArgs a) {
+  using C = Bf16Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char ksm[2][C::KTILEB];
+  __shared__ __attribute__((aligned(16))) char vsm[2][C::VTILEB];
+  const int nkv = a.sk_nkv;
+  const int cu = xcd_tile_order(blockIdx.x, gridDim.x);
+  const long W = (long)a.sk_tiles * nkv;
+  const long hi = W * (cu + 1) / gridDim.x;
+  long pos = W * cu / gridDim.x;
   const int first = (int)(pos / nkv);
   while (pos < hi) {
-    int tile_g, slot = -1, piece = 0, k0 = -1, k1 = -1;
-    long next = hi;
-    if (sk) {
-      tile_g = (int)(pos / nkv);
-      next = hi < (long)(tile_g + 1) * nkv ? hi : (long)(tile_g + 1) * nkv;
-      k0 = (int)(pos - (long)tile_g * nkv);
-      k1 = (int)(next - (long)tile_g * nkv);
-      if (k0 != 0 || k1 != nkv) slot = 2 * cu + (tile_g == first ? 0 : 1);
-    } else if ((int)blockIdx.x < a.whole) {
-      tile_g = a.tile_order != nullptr ? a.tile_order[blockIdx.x] : xcd_tile_order(blockIdx.x, a.whole);
-    } else {
-      // pieces of neighbouring tiles on one XCD, like the whole tiles
-      slot = xcd_tile_order(blockIdx.x - a.whole, gridDim.x - a.whole);
-      tile_g = a.whole + slot / a.split;
-      if (a.tile_order != nullptr) tile_g = a.tile_order[tile_g];
-      piece = slot % a.split;
-    }
-    fwd_tile<D, SPARSE>(a, ksm, vsm, tile_g, slot, piece, k0, k1);
+    const int tile_g = (int)(pos / nkv);
+    const long next = hi < (long)(tile_g + 1) * nkv ? hi : (long)(tile_g + 1) * nkv;
+    const int k0 = (int)(pos - (long)tile_g * nkv), k1 = (int)(next - (long)tile_g * nkv);
+    const int slot = (k0 != 0 || k1 != nkv) ? 2 * cu + (tile_g == first ? 0 : 1) : -1;
+    fwd_tile<D, false>(a, ksm, vsm, tile_g, slot, 0, k0, k1);
     pos = next;
     if (pos < hi) __syncthreads();  // the next piece reuses the LDS buffers
   }
@@ -681,6 +688,15 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch
   args.sk_tiles = sch.sk_tiles;
   args.sk_cus = sch.sk_cus;
   const bool sparse = a.kv_list != nullptr;
+  if (sch.sk_nkv > 0 && !sparse) {
+    if (head_dim == 128)
+      hipLaunchKernelGGL(attn_fwd_bf16_persistent_kernel<128>, dim3(sch.grid), dim3(Bf16Cfg<128>::NT), 0, stream, args);
+    else if (head_dim == 64)
+      hipLaunchKernelGGL(attn_fwd_bf16_persistent_kernel<64>, dim3(sch.grid), dim3(Bf16Cfg<64>::NT), 0, stream, args);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (head_dim == 128 && !sparse)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), dim3(sch.grid), dim3(Bf16Cfg<128>::NT), 0, stream, args);
   else if (head_dim == 128)
