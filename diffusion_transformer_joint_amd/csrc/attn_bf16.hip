@@ -28,7 +28,7 @@
 //   tiles form p = exp2(c s - m) directly and only move m (rescaling O and l)
 //   when a row's tile sum reaches 2^32.  The result is the same softmax.
 //
-// Layouts: q, k, v, o [B][N][H][D] bf16; rope [N][D/2] float2 (cos, sin).
+// Layouts: q, k, v, o [B][N][H][D] bf16; rope [N][D/2] packed fp16 (cos, sin).
 #include "attn_common.h"
 #include "device_common.h"
 #include "kernels.h"
@@ -68,7 +68,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
   const int tile = tile_g - a.rng_tile0[rg];
   const int q_tiles = (N + C::BM - 1) / C::BM;
   const int n_tiles = (N + C::BN - 1) / C::BN;
-  const float2* const rope = a.rope + (size_t)tok0 * (D / 2);
+  const uint32_t* const rope = a.rope + (size_t)tok0 * (D / 2);
   // The 64-key tiles this query tile attends to, by position p: all of them
   // (p itself), or in a tile-sparse launch the kept list.  A split piece runs
   // positions [kv0, kv1).  Positions past the range map to a tile past N,
@@ -120,7 +120,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
   const int st_chunk = tid % C::CPR;
   const int st_row0 = tid / C::CPR;
   u32x4 kraw[C::NPASS], vraw[C::NPASS];
-  f32x4 kcs[C::NPASS][2];
+  u32x4 kcs[C::NPASS];  // table entries of the 4 pairs of each slot
   // Buffer loads relative to the tile's first row: rows at or past N read as
   // zero (their keys are masked to -inf before the softmax), and tiles past
   // the last one are staged as zeros into a buffer that is never read.  The
@@ -131,7 +131,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
   for (int p = 0; p < C::NPASS; ++p) {
     const int r = st_row0 + p * C::RPP;
     kv_off[p] = (uint32_t)(r * tok_stride * 2 + st_chunk * 16);
-    rp_off[p] = (uint32_t)(r * (D / 2) * 8 + st_chunk * 32);
+    rp_off[p] = (uint32_t)(r * (D / 2) * 4 + st_chunk * 16);
   }
   auto tile_bytes = [&](int kt0) -> uint32_t {
     const int rows = N - kt0;
@@ -139,14 +139,13 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
   };
   auto load_k = [&](int kt0) {
     const int rows = N - kt0;
-    const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 8) : 0u;
+    const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 4) : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, tile_bytes(kt0));
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(rope + (size_t)kt0 * (D / 2), rp_bytes);
 #pragma unroll
     for (int p = 0; p < C::NPASS; ++p) {
       kraw[p] = buffer_load_b128(rk, kv_off[p]);
-      kcs[p][0] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off[p]));
-      kcs[p][1] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off[p] + 16));
+      kcs[p] = buffer_load_b128(rr, rp_off[p]);
     }
   };
   auto load_v = [&](int kt0) {
@@ -158,7 +157,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
     FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
 #pragma unroll
     for (int p = 0; p < C::NPASS; ++p)
-      lds_write_b128(kl + k_off<D>(st_row0 + p * C::RPP, st_chunk), rope_chunk(kraw[p], kcs[p][0], kcs[p][1]));
+      lds_write_b128(kl + k_off<D>(st_row0 + p * C::RPP, st_chunk), rope_chunk(kraw[p], kcs[p]));
   };
   auto store_v = [&](int buf) {
     FLUX_LDS char* vl = (FLUX_LDS char*)vsm[buf];
@@ -183,15 +182,14 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
                   "Q staging fits the K and V buffers");
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + (size_t)qt * C::BM * tok_stride, tile_bytes(qt * C::BM));
     const __amdgpu_buffer_rsrc_t rqa =
-        make_rsrc(rope + (size_t)qt * C::BM * (D / 2), (uint32_t)((N - qt * C::BM) * (D / 2) * 8));
+        make_rsrc(rope + (size_t)qt * C::BM * (D / 2), (uint32_t)((N - qt * C::BM) * (D / 2) * 4));
     u32x4 qraw[QCH];
-    f32x4 qcs[QCH][2];
+    u32x4 qcs[QCH];
 #pragma unroll
     for (int i = 0; i < QCH; ++i) {
       const int r = st_row0 + i * C::RPP;
       qraw[i] = buffer_load_b128(rq, (uint32_t)(r * tok_stride * 2 + st_chunk * 16));
-      qcs[i][0] = __builtin_bit_cast(f32x4, buffer_load_b128(rqa, (uint32_t)(r * (D / 2) * 8 + st_chunk * 32)));
-      qcs[i][1] = __builtin_bit_cast(f32x4, buffer_load_b128(rqa, (uint32_t)(r * (D / 2) * 8 + st_chunk * 32 + 16)));
+      qcs[i] = buffer_load_b128(rqa, (uint32_t)(r * (D / 2) * 4 + st_chunk * 16));
     }
     if (kv0 < kv1) {
       load_k(kvt(kv0) * C::BN);
@@ -204,7 +202,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
 #pragma unroll
     for (int i = 0; i < QCH; ++i) {
       const int r = st_row0 + i * C::RPP;
-      lds_write_b128(qrow_lds(r) + 16 * st_chunk, rope_chunk_scaled(qraw[i], qcs[i][0], qcs[i][1], c));
+      lds_write_b128(qrow_lds(r) + 16 * st_chunk, rope_chunk_scaled(qraw[i], qcs[i], c));
     }
     __syncthreads();
     const FLUX_LDS char* ql = qrow_lds(wave * 32 + l32);
@@ -366,10 +364,6 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
   // read NPF MFMAs ahead and a slice of independent VALU work: RoPE + store of
   // K(t+1) and store of V(t) beside QK, P(t) beside PV once the P(t-1)
   // fragment it replaces has been consumed.
-  auto rope_pair = [&](uint32_t x, float cc, float ss) -> uint32_t {
-    const float x0 = bf16lo(x), x1 = bf16hi(x);
-    return pack_bf16(x0 * cc - x1 * ss, x0 * ss + x1 * cc);
-  };
   auto p_pair = [&](float x0, float x1, float& bsum) -> uint32_t {
     bf16x2 q2;
     q2[0] = (__bf16)__builtin_amdgcn_exp2f(x0);
@@ -429,8 +423,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
       }
       if constexpr (j < ROPE_END && j % 2 == 0) {  // RoPE of K(t+1), one pair
         constexpr int p = (j / 2) >> 2, e = (j / 2) & 3;
-        const f32x4 cs = kcs[p][e >> 1];
-        kr[p][e] = rope_pair(kraw[p][e], cs[2 * (e & 1)], cs[2 * (e & 1) + 1]);
+        kr[p][e] = rope_pair(kraw[p][e], kcs[p][e]);
         if constexpr (e == 3) lds_write_b128(kw + k_off<D>(st_row0 + p * C::RPP, st_chunk), kr[p]);
       }
       if constexpr (j == VST0 || j == VST1) {     // V(t)

@@ -65,10 +65,10 @@ template <> __device__ __forceinline__ int swz<128>(int r) { return ((r & 3) << 
 // the half; bits 1..3 pick the chunk within it.
 template <> __device__ __forceinline__ int swz<64>(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
-// R^T on a pair: rotation by the negative angle.
-__device__ __forceinline__ void rot_back(float& x0, float& x1, float2 cs) {
-  const float a = x0 * cs.x + x1 * cs.y;
-  const float b = x1 * cs.x - x0 * cs.y;
+// R^T on a pair (rotation by the negative angle), table entry w.
+__device__ __forceinline__ void rot_back(float& x0, float& x1, uint32_t w) {
+  float a, b;
+  rot_pair_back(x0, x1, w, a, b);
   x0 = a;
   x1 = b;
 }
@@ -250,10 +250,9 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdArgs a) {
     i = (row / a.heads) % a.n_tokens;
     b = row / (a.heads * a.n_tokens);
     const size_t off = (size_t)row * D + 8 * cc;
-    const f32x4* rp = (const f32x4*)(a.rope + (size_t)i * (D / 2) + 4 * cc);
-    const f32x4 cs01 = rp[0], cs23 = rp[1];
-    *(u32x4*)(a.qr + off) = rope_chunk(global_load_b128(a.q + off), cs01, cs23);
-    *(u32x4*)(a.kr + off) = rope_chunk(global_load_b128(a.k + off), cs01, cs23);
+    const u32x4 cs = *(const u32x4*)(a.rope + (size_t)i * (D / 2) + 4 * cc);
+    *(u32x4*)(a.qr + off) = rope_chunk(global_load_b128(a.q + off), cs);
+    *(u32x4*)(a.kr + off) = rope_chunk(global_load_b128(a.k + off), cs);
     const u32x4 x = global_load_b128(a.dout + off);
     const u32x4 y = global_load_b128(a.out + off);
 #pragma unroll
@@ -299,15 +298,13 @@ __device__ __forceinline__ void bwd_dq(const BwdArgs& a, int blk, FLUX_LDS char*
   for (int t = 0; t < C::KSTEPS; ++t) {
     const int d0 = 16 * t + 8 * g;
     u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    f32x4 cs01 = {1.f, 0.f, 1.f, 0.f}, cs23 = {1.f, 0.f, 1.f, 0.f};
+    u32x4 cs = {0, 0, 0, 0};  // rows past N: zeros rotate to zeros
     if (qok) {
       x = global_load_b128(a.q + base + (size_t)qrow * ts + d0);
       y = global_load_b128(a.dout + base + (size_t)qrow * ts + d0);
-      const f32x4* rp = (const f32x4*)(a.rope + (size_t)qrow * (D / 2) + d0 / 2);
-      cs01 = rp[0];
-      cs23 = rp[1];
+      cs = *(const u32x4*)(a.rope + (size_t)qrow * (D / 2) + d0 / 2);
     }
-    qf[t] = __builtin_bit_cast(bf16x8, rope_chunk_scaled(x, cs01, cs23, c));
+    qf[t] = __builtin_bit_cast(bf16x8, rope_chunk_scaled(x, cs, c));
     of[t] = __builtin_bit_cast(bf16x8, y);
   }
   const size_t row_bh = ((size_t)b * H + h) * N;
@@ -371,7 +368,7 @@ __device__ __forceinline__ void bwd_dq(const BwdArgs& a, int blk, FLUX_LDS char*
   // epilogue: dq = R^T (scale dQ~), bf16
   if (qok) {
     uint16_t* orow = a.dq + base + (size_t)qrow * ts;
-    const float2* rp = a.rope + (size_t)qrow * (D / 2);
+    const uint32_t* rp = a.rope + (size_t)qrow * (D / 2);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -446,15 +443,13 @@ __device__ __forceinline__ void bwd_dkv(const BwdArgs& a, int blk, FLUX_LDS char
   for (int t = 0; t < C::KSTEPS; ++t) {
     const int d0 = 16 * t + 8 * g;
     u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
-    f32x4 cs01 = {1.f, 0.f, 1.f, 0.f}, cs23 = {1.f, 0.f, 1.f, 0.f};
+    u32x4 cs = {0, 0, 0, 0};  // rows past N: zeros rotate to zeros
     if (kok) {
       x = global_load_b128(a.k + base + (size_t)krow * ts + d0);
       if constexpr (DK) y = global_load_b128(a.v + base + (size_t)krow * ts + d0);
-      const f32x4* rp = (const f32x4*)(a.rope + (size_t)krow * (D / 2) + d0 / 2);
-      cs01 = rp[0];
-      cs23 = rp[1];
+      cs = *(const u32x4*)(a.rope + (size_t)krow * (D / 2) + d0 / 2);
     }
-    kf[t] = __builtin_bit_cast(bf16x8, rope_chunk_scaled(x, cs01, cs23, c));
+    kf[t] = __builtin_bit_cast(bf16x8, rope_chunk_scaled(x, cs, c));
     if constexpr (DK) vf[t] = __builtin_bit_cast(bf16x8, y);
   }
   const TileOffsets<D> off(lane);
@@ -492,7 +487,7 @@ __device__ __forceinline__ void bwd_dkv(const BwdArgs& a, int blk, FLUX_LDS char
   // epilogue: dk = R^T (scale dK~) or dv, bf16
   if (kok) {
     uint16_t* orow = (DK ? a.dk : a.dv) + base + (size_t)krow * ts;
-    const float2* rp = a.rope + (size_t)krow * (D / 2);
+    const uint32_t* rp = a.rope + (size_t)krow * (D / 2);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll

@@ -1,5 +1,5 @@
-// Pieces shared by the bf16 and e4m3 attention kernels: LDS row layout,
-// key-row permutation of the score MFMA, RoPE of a 16-byte bf16 chunk and the
+// Pieces shared by the attention kernels: LDS row layout, key-row
+// permutation of the score MFMA, RoPE from the packed fp16 table and the
 // MFMA/VALU interleave hint.
 #pragma once
 #include "device_common.h"
@@ -44,29 +44,59 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
-// Rotate the 4 adjacent bf16 pairs of one 16-byte chunk by (cos, sin).
-__device__ __forceinline__ u32x4 rope_chunk(u32x4 x, f32x4 cs01, f32x4 cs23) {
+// RoPE table entries are packed fp16 pairs: cos in the low half, sin in the
+// high half (rope_table.hip).  The rotation's products take the fp16 values
+// as operands of mixed-precision FMAs (v_fma_mix_f32 widens them exactly), so
+// the half-size table costs no conversion instructions; a zero addend keeps
+// a plain product in FMA form for that.  The halves are read through 16-bit
+// integers: a bit cast of one vector element to a two-half vector made the
+// compiler narrow a 16-byte table load to its first dword and use that entry
+// for every pair.
+__device__ __forceinline__ float cs_cos(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float cs_sin(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// (x0 c - x1 s, x0 s + x1 c) in fp32 from the table entry w.
+__device__ __forceinline__ void rot_pair(float x0, float x1, uint32_t w, float& y0, float& y1) {
+  const float c = cs_cos(w), s = cs_sin(w);
+  y0 = __builtin_fmaf(x0, c, __builtin_fmaf(-x1, s, 0.f));
+  y1 = __builtin_fmaf(x0, s, __builtin_fmaf(x1, c, 0.f));
+}
+
+// The inverse rotation (x0 c + x1 s, x1 c - x0 s).
+__device__ __forceinline__ void rot_pair_back(float x0, float x1, uint32_t w, float& y0, float& y1) {
+  const float c = cs_cos(w), s = cs_sin(w);
+  y0 = __builtin_fmaf(x0, c, __builtin_fmaf(x1, s, 0.f));
+  y1 = __builtin_fmaf(x1, c, __builtin_fmaf(-x0, s, 0.f));
+}
+
+// One bf16 pair rotated and rounded back to bf16.
+__device__ __forceinline__ uint32_t rope_pair(uint32_t x, uint32_t w) {
+  float y0, y1;
+  rot_pair(bf16lo(x), bf16hi(x), w, y0, y1);
+  return pack_bf16(y0, y1);
+}
+
+// The 4 adjacent bf16 pairs of one 16-byte chunk, with their 4 table entries.
+__device__ __forceinline__ u32x4 rope_chunk(u32x4 x, u32x4 w) {
   u32x4 y;
-  float c[4] = {cs01[0], cs01[2], cs23[0], cs23[2]};
-  float s[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float x0 = bf16lo(x[i]), x1 = bf16hi(x[i]);
-    y[i] = pack_bf16(x0 * c[i] - x1 * s[i], x0 * s[i] + x1 * c[i]);
-  }
+  for (int i = 0; i < 4; ++i) y[i] = rope_pair(x[i], w[i]);
   return y;
 }
 
 // Same rotation, result multiplied by k before rounding (Q carries the
 // softmax scale times log2(e)).
-__device__ __forceinline__ u32x4 rope_chunk_scaled(u32x4 x, f32x4 cs01, f32x4 cs23, float k) {
+__device__ __forceinline__ u32x4 rope_chunk_scaled(u32x4 x, u32x4 w, float k) {
   u32x4 y;
-  float c[4] = {cs01[0], cs01[2], cs23[0], cs23[2]};
-  float s[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float x0 = bf16lo(x[i]), x1 = bf16hi(x[i]);
-    y[i] = pack_bf16((x0 * c[i] - x1 * s[i]) * k, (x0 * s[i] + x1 * c[i]) * k);
+    float y0, y1;
+    rot_pair(bf16lo(x[i]), bf16hi(x[i]), w[i], y0, y1);
+    y[i] = pack_bf16(y0 * k, y1 * k);
   }
   return y;
 }

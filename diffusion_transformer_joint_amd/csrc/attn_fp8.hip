@@ -59,29 +59,22 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
   return (uint32_t)w;
 }
 
-// Rotate the 8 pairs of 16 codes x (dword-packed) by (cos, sin) in cs[0..3]
-// (two pairs per f32x4) and return the halved result as e4m3 codes.
-__device__ __forceinline__ u32x4 rope16_e4m3(u32x4 x, const f32x4* cs) {
-  u32x4 y;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float f[4];
-    e4m3x4_to_f32(x[i], f);
-    // pairs (f0, f1) and (f2, f3); angles 2i and 2i+1 of the chunk
-    const float c0 = 0.5f * cs[i][0], s0 = 0.5f * cs[i][1];
-    const float c1 = 0.5f * cs[i][2], s1 = 0.5f * cs[i][3];
-    y[i] = f32x4_to_e4m3(f[0] * c0 - f[1] * s0, f[0] * s0 + f[1] * c0, f[2] * c1 - f[3] * s1, f[2] * s1 + f[3] * c1);
-  }
-  return y;
+// One dword of codes (two pairs) rotated by table entries w0, w1 and halved.
+__device__ __forceinline__ uint32_t rope_dword_e4m3(uint32_t x, uint32_t w0, uint32_t w1) {
+  float f[4], y[4];
+  e4m3x4_to_f32(x, f);
+  rot_pair(f[0], f[1], w0, y[0], y[1]);
+  rot_pair(f[2], f[3], w1, y[2], y[3]);
+  return f32x4_to_e4m3(0.5f * y[0], 0.5f * y[1], 0.5f * y[2], 0.5f * y[3]);
 }
 
-// One dword of codes (two pairs) rotated by cs = (c0, s0, c1, s1), halved.
-__device__ __forceinline__ uint32_t rope_dword_e4m3(uint32_t x, f32x4 cs) {
-  float f[4];
-  e4m3x4_to_f32(x, f);
-  const float c0 = 0.5f * cs[0], s0 = 0.5f * cs[1];
-  const float c1 = 0.5f * cs[2], s1 = 0.5f * cs[3];
-  return f32x4_to_e4m3(f[0] * c0 - f[1] * s0, f[0] * s0 + f[1] * c0, f[2] * c1 - f[3] * s1, f[2] * s1 + f[3] * c1);
+// The 8 pairs of 16 codes x (dword-packed) rotated by their table entries
+// w[0] (pairs 0-3) and w[1] (pairs 4-7), halved, as e4m3 codes.
+__device__ __forceinline__ u32x4 rope16_e4m3(u32x4 x, const u32x4 (&w)[2]) {
+  u32x4 y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = rope_dword_e4m3(x[i], w[i >> 1][2 * (i & 1)], w[i >> 1][2 * (i & 1) + 1]);
+  return y;
 }
 
 // 16 codes to 16 bf16 (exact): two 16-byte halves.
@@ -140,12 +133,13 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
     for (int hf = 0; hf < 2; ++hf) {
       const int d0 = 64 * t + 32 * g + 16 * hf;
       u32x4 x = {0, 0, 0, 0};
-      f32x4 cs[4] = {{1.f, 0.f, 1.f, 0.f}, {1.f, 0.f, 1.f, 0.f}, {1.f, 0.f, 1.f, 0.f}, {1.f, 0.f, 1.f, 0.f}};
+      constexpr uint32_t kIdentity = 0x3C00u;  // cos 1, sin 0 (fp16)
+      u32x4 cs[2] = {{kIdentity, kIdentity, kIdentity, kIdentity}, {kIdentity, kIdentity, kIdentity, kIdentity}};
       if (qrow < N) {
         x = global_load_b128(qbase + (size_t)qrow * tok_stride + d0);
-        const f32x4* rp = (const f32x4*)(a.rope + (size_t)qrow * (D / 2) + d0 / 2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cs[i] = rp[i];
+        const u32x4* rp = (const u32x4*)(a.rope + (size_t)qrow * (D / 2) + d0 / 2);
+        cs[0] = rp[0];
+        cs[1] = rp[1];
       }
       y[hf] = rope16_e4m3(x, cs);
     }
@@ -157,19 +151,19 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   const bool st_on = C::NCH >= C::NT || tid < C::NCH;  // every thread stages when D = 128
   const int st_row = tid / C::CPR8, st_c = tid % C::CPR8;
   const uint32_t kv_off = (uint32_t)(st_row * tok_stride + st_c * 16);
-  const uint32_t rp_off = (uint32_t)(st_row * (D / 2) * 8 + st_c * 64);
+  const uint32_t rp_off = (uint32_t)(st_row * (D / 2) * 4 + st_c * 32);
   u32x4 kraw, vraw;
-  f32x4 kcs[4];
+  u32x4 kcs[2];
   auto stage_load_k = [&](int kt0) {
     if (!st_on) return;
     const int rows = N - kt0;
     const uint32_t kv_bytes = rows > 0 ? (uint32_t)((rows - 1) * tok_stride + D) : 0u;
-    const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 8) : 0u;
+    const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 4) : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, kv_bytes);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rope + (size_t)kt0 * (D / 2), rp_bytes);
     kraw = buffer_load_b128(rk, kv_off);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kcs[i] = __builtin_bit_cast(f32x4, buffer_load_b128(rr, rp_off + 16 * i));
+    for (int i = 0; i < 2; ++i) kcs[i] = buffer_load_b128(rr, rp_off + 16 * i);
   };
   auto stage_load_v = [&](int kt0) {
     if (!st_on) return;
@@ -363,7 +357,7 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
       // widened and stored; loads of K(t+2) and V(t+1)
       constexpr int R0 = NK;  // first staging slot
       if constexpr (j >= R0 && j < R0 + 4) {
-        if (st_on) ky[j - R0] = rope_dword_e4m3(kraw[j - R0], kcs[j - R0]);
+        if (st_on) ky[j - R0] = rope_dword_e4m3(kraw[j - R0], kcs[(j - R0) >> 1][2 * ((j - R0) & 1)], kcs[(j - R0) >> 1][2 * ((j - R0) & 1) + 1]);
         if constexpr (j == R0 + 3) {
           if (st_on) lds_write_b128(kw + st_row * C::K8ROW + st_c * 16, ky);
         }

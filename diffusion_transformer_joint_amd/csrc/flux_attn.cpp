@@ -60,7 +60,10 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 struct flux_attn_plan {
   flux_attn_config cfg;
   int device = -1;
-  float2* rope_table = nullptr;  // [max_tokens][head_dim/2]
+  // RoPE table, [max_tokens][head_dim/2], rewritten by each call: packed fp16
+  // (cos, sin) for the attention kernels, or fp32 pairs for the tile-mask
+  // rule (the allocation is sized for the latter).
+  void* rope_table = nullptr;
   double* freq = nullptr;        // [head_dim/2]
   float* part_o = nullptr;       // split-K/V partials: [max_pieces][256][head_dim]
   float2* part_ml = nullptr;     // [max_pieces][256]
@@ -81,6 +84,9 @@ struct flux_attn_plan {
 };
 
 namespace {
+
+// The RoPE table in the attention kernels' form (packed fp16 pairs).
+uint32_t* rope16(flux_attn_plan* p) { return static_cast<uint32_t*>(p->rope_table); }
 
 void release_timing(flux_attn_plan* p) {
   for (auto e : p->ev_start) (void)hipEventDestroy(e);
@@ -346,7 +352,7 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
   if (dev != plan->device)
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan was created on device %d, current device is %d", plan->device, dev);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  e = flux::launch_rope_table(pos_ids, plan->freq, plan->rope_table, n, c.head_dim, c.rope_axes_dim[0],
+  e = flux::launch_rope_table(pos_ids, plan->freq, rope16(plan), n, c.head_dim, c.rope_axes_dim[0],
                               c.rope_axes_dim[1], stream);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   const float scale = c.softmax_scale > 0.0f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
@@ -413,7 +419,7 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
       f.v = static_cast<const uint8_t*>(v) + off * tok;
       f.scales = qkv_scale;
       f.o = static_cast<uint16_t*>(out) + off * tok;
-      f.rope = plan->rope_table + off * (c.head_dim / 2);
+      f.rope = rope16(plan) + off * (c.head_dim / 2);
       f.n_tokens = gl[0];
       f.batch_tokens = n;
       f.heads = c.num_heads;
@@ -432,7 +438,7 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
       a.k = static_cast<const uint16_t*>(k);
       a.v = static_cast<const uint16_t*>(v);
       a.o = static_cast<uint16_t*>(out);
-      a.rope = plan->rope_table;
+      a.rope = rope16(plan);
       e = flux::launch_attn_bf16(a, c.head_dim, sch, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -500,7 +506,7 @@ int flux_attn_backward(flux_attn_plan* plan, const void* q, const void* k, const
   if (dev != plan->device)
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan was created on device %d, current device is %d", plan->device, dev);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  e = flux::launch_rope_table(pos_ids, plan->freq, plan->rope_table, n, c.head_dim, c.rope_axes_dim[0],
+  e = flux::launch_rope_table(pos_ids, plan->freq, rope16(plan), n, c.head_dim, c.rope_axes_dim[0],
                               c.rope_axes_dim[1], stream);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   const float scale = c.softmax_scale > 0.0f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
@@ -517,7 +523,7 @@ int flux_attn_backward(flux_attn_plan* plan, const void* q, const void* k, const
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  a.rope = plan->rope_table;
+  a.rope = rope16(plan);
   a.n_tokens = n;
   a.heads = c.num_heads;
   a.batch = c.batch;
@@ -581,15 +587,16 @@ int flux_attn_block_mask(flux_attn_plan* plan, const void* q, const void* k, con
   if (!(tau > 0.0f && tau <= 1.0f)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "tau must be in (0, 1]");
   const flux_attn_config& c = plan->cfg;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = flux::launch_rope_table(pos_ids, plan->freq, plan->rope_table, n, c.head_dim, c.rope_axes_dim[0],
-                                         c.rope_axes_dim[1], stream);
+  float2* const table = static_cast<float2*>(plan->rope_table);
+  hipError_t e = flux::launch_rope_table_f32(pos_ids, plan->freq, table, n, c.head_dim, c.rope_axes_dim[0],
+                                             c.rope_axes_dim[1], stream);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   const int QT = (n + 255) / 256, KT = (n + 63) / 64;
-  e = flux::launch_tile_means(static_cast<const uint16_t*>(q), plan->rope_table, plan->qbar, n, n, c.num_heads,
-                              c.batch, c.head_dim, 256, stream);
+  e = flux::launch_tile_means(static_cast<const uint16_t*>(q), table, plan->qbar, n, n, c.num_heads, c.batch,
+                              c.head_dim, 256, stream);
   if (e == hipSuccess)
-    e = flux::launch_tile_means(static_cast<const uint16_t*>(k), plan->rope_table, plan->kbar, n, n, c.num_heads,
-                                c.batch, c.head_dim, 64, stream);
+    e = flux::launch_tile_means(static_cast<const uint16_t*>(k), table, plan->kbar, n, n, c.num_heads, c.batch,
+                                c.head_dim, 64, stream);
   if (e == hipSuccess)
     e = flux::launch_block_select(plan->qbar, plan->kbar, mask, c.batch * c.num_heads * QT, QT, KT, c.head_dim,
                                   plan_c(c), std::log2(tau), stream);
@@ -605,7 +612,7 @@ int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k,
   if (st) return st;
   const flux_attn_config& c = plan->cfg;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = flux::launch_rope_table(pos_ids, plan->freq, plan->rope_table, n, c.head_dim, c.rope_axes_dim[0],
+  hipError_t e = flux::launch_rope_table(pos_ids, plan->freq, rope16(plan), n, c.head_dim, c.rope_axes_dim[0],
                                          c.rope_axes_dim[1], stream);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   const int QT = (n + 255) / 256, KT = (n + 63) / 64;
@@ -625,7 +632,7 @@ int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k,
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.o = static_cast<uint16_t*>(out);
-  a.rope = plan->rope_table;
+  a.rope = rope16(plan);
   {
     const int t0 = 0;
     set_ranges(a, &t0, &n, 1, c.batch, c.num_heads);

@@ -10,7 +10,7 @@ struct AttnArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;            // [B][N][H][D] bf16 bits
-  const float2* rope;     // [N][D/2] (cos, sin)
+  const uint32_t* rope;   // [N][D/2] (cos, sin) as packed fp16, cos in the low half
   int batch_tokens;       // tokens between consecutive batch entries of q, k, v, o
   int heads;
   int batch;
@@ -72,7 +72,7 @@ struct Fp8Args {
   const uint8_t* v;
   const float* scales;    // [3][B][H]: q, k, v scales
   uint16_t* o;            // [B][N][H][D] bf16 bits
-  const float2* rope;     // [N][D/2]
+  const uint32_t* rope;   // [N][D/2] packed fp16 (cos, sin)
   int n_tokens;
   int batch_tokens;
   int heads;
@@ -85,9 +85,13 @@ struct Fp8Args {
   float2* part_ml;
 };
 
-// (cos, sin) of pos[n][axis(p)] * freq[p] for every token n and pair p.
-hipError_t launch_rope_table(const int32_t* pos, const double* freq, float2* table, int n_tokens,
+// (cos, sin) of pos[n][axis(p)] * freq[p] for every token n and pair p, as
+// packed fp16 (cos in the low half).
+hipError_t launch_rope_table(const int32_t* pos, const double* freq, uint32_t* table, int n_tokens,
                              int head_dim, int d0, int d1, hipStream_t stream);
+// The same angles as fp32 (cos, sin) pairs, for the tile-mask rule.
+hipError_t launch_rope_table_f32(const int32_t* pos, const double* freq, float2* table, int n_tokens,
+                                 int head_dim, int d0, int d1, hipStream_t stream);
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream);
 
@@ -105,7 +109,7 @@ struct BwdArgs {
   uint16_t* dq;           // [B][N][H][D] bf16
   uint16_t* dk;
   uint16_t* dv;
-  const float2* rope;     // [N][D/2] (cos, sin)
+  const uint32_t* rope;   // [N][D/2] packed fp16 (cos, sin)
   int n_tokens;
   int heads;
   int batch;

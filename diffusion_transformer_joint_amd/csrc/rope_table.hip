@@ -5,13 +5,22 @@
 // GPUs", How it works).  Multi-axis form: head_dim is cut into three slices of
 // widths (d0, d1, d2); pair j of slice a is rotated by pos[n][a] * theta^(-2j/d_a).
 // The per-pair frequencies are computed once per plan on the host in double;
-// here each angle is formed and evaluated in double, then stored as float.
+// here each angle is formed and evaluated in double.
+//
+// Two storage forms:
+//   packed fp16 (the attention kernels): one dword per pair, cos in the low
+//     half and sin in the high half, each rounded to nearest from double:
+//     4 bytes per pair, error at most 2^-12 in each, a small fraction of the
+//     bf16 rounding that follows the rotation;
+//   float2 (the tile-mask rule, whose pooled scores decide kept tiles and are
+//     compared with an exact rule): (cos, sin) as fp32.
 #include "kernels.h"
 
 namespace flux {
 
+template <bool PACKED16>
 __global__ void rope_table_kernel(const int32_t* __restrict__ pos, const double* __restrict__ freq,
-                                  float2* __restrict__ table, int n_tokens, int half, int p0, int p1) {
+                                  void* __restrict__ table, int n_tokens, int half, int p0, int p1) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n_tokens * half) return;
   const int n = idx / half, p = idx - n * half;
@@ -19,17 +28,34 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ pos, const double*
   const double ang = (double)pos[3 * n + axis] * freq[p];
   double s, c;
   sincos(ang, &s, &c);
-  table[idx] = make_float2((float)c, (float)s);
+  if constexpr (PACKED16) {
+    const uint32_t ch = __builtin_bit_cast(uint16_t, (_Float16)c);
+    const uint32_t sh = __builtin_bit_cast(uint16_t, (_Float16)s);
+    static_cast<uint32_t*>(table)[idx] = ch | (sh << 16);
+  } else {
+    static_cast<float2*>(table)[idx] = make_float2((float)c, (float)s);
+  }
 }
 
-hipError_t launch_rope_table(const int32_t* pos, const double* freq, float2* table, int n_tokens,
-                             int head_dim, int d0, int d1, hipStream_t stream) {
+template <bool PACKED16>
+static hipError_t launch_table(const int32_t* pos, const double* freq, void* table, int n_tokens, int head_dim,
+                               int d0, int d1, hipStream_t stream) {
   const int half = head_dim / 2;
   const int total = n_tokens * half;
   const int threads = 256;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((total + threads - 1) / threads), dim3(threads), 0, stream,
+  hipLaunchKernelGGL(rope_table_kernel<PACKED16>, dim3((total + threads - 1) / threads), dim3(threads), 0, stream,
                      pos, freq, table, n_tokens, half, d0 / 2, d1 / 2);
   return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const int32_t* pos, const double* freq, uint32_t* table, int n_tokens,
+                             int head_dim, int d0, int d1, hipStream_t stream) {
+  return launch_table<true>(pos, freq, table, n_tokens, head_dim, d0, d1, stream);
+}
+
+hipError_t launch_rope_table_f32(const int32_t* pos, const double* freq, float2* table, int n_tokens,
+                                 int head_dim, int d0, int d1, hipStream_t stream) {
+  return launch_table<false>(pos, freq, table, n_tokens, head_dim, d0, d1, stream);
 }
 
 }  // namespace flux

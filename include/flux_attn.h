@@ -94,7 +94,7 @@ int flux_attn_validate_forward(const flux_attn_config* cfg, const void* q, const
                                const int32_t* pos_ids, const void* out, int32_t mode);
 
 /* Creates a plan on the current HIP device: validates cfg and allocates the
- * plan's device workspace once (RoPE table of max_tokens x head_dim/2 float2,
+ * plan's device workspace once (RoPE table of max_tokens x head_dim/2 x 8 bytes,
  * split-K/V partials; for bf16 plans also the tile-sparse tile means and
  * kept-tile lists, and the backward's row sums and rotated copies of q and k:
  * 2 x batch x max_tokens x num_heads x head_dim bf16).  *out receives the plan, or

@@ -11,23 +11,27 @@ such rounded products, so their relative L2 error is a small multiple of the
 forward's; the bound used is relative L2 <= 1.5e-2 per gradient (three times
 the forward's 5e-3).
 
-The log-sum-exp is checked twice.  (1) Against the same formula evaluated in
-fp64 on the score operands the kernel multiplies: bf16 RNE of c R(q) (c = scale
-log2 e) and of R(k), with R from the oracle.  What is left is l, the fp32 sum
-of the bf16-rounded p (each within 2^-9 relative): 2.5e-3; and the kernel
-rotates in fp32, so now and then an operand lands one bf16 ulp away from the
-fp64-rotated value, moving one product a_d b_d by up to 2^-8 of itself: plus
-2^-8 ln 2 max_jd |a_d b_d| per row.  (2) Against
-the exact oracle value, with the bound that rounding the two operands (2^-9
-relative each) puts on every score: |d lse| <= max_j |d s_ij| <= (2^-8 + 2^-18)
-ln 2 sum_d |(c R(q))_d R(k)_d| (the log-sum-exp is 1-Lipschitz in the largest
-score change), plus the 2.5e-3 of (1).
+The log-sum-exp is checked twice.  The kernel's score operands are bf16 RNE
+of c R16(q) (c = scale log2 e) and of R16(k), where R16 rotates in fp32 with
+cos and sin rounded to fp16 (the library's RoPE table).  (1) Against the same
+formula evaluated in fp64 on those operands, with R16 from fp16-rounded oracle
+angles.  What is left is l, the fp32 sum of the bf16-rounded p (each within
+2^-9 relative): 2.5e-3; and fp32 versus fp64 rotation arithmetic, which now
+and then puts an operand one bf16 ulp away, moving one product a_d b_d by up
+to 2^-8 of itself: plus 2^-8 ln 2 max_jd |a_d b_d| per row.  (2) Against the
+exact oracle value.  Each operand is off by at most 2^-9 of itself (bf16)
+plus the angle term e = (2^-12 + 2^-22)(|x0| + |x1|) per pair component
+(fp16 cos and sin are within 2^-12; the slack covers the fp32 arithmetic),
+so every score moves by at most sum_d (da |b_d| + |a_d| db + da db) with
+da = 2^-9 (|a_d| + e_d) + e_d, and the log-sum-exp, 1-Lipschitz in the
+largest score change, by at most ln 2 times that; plus the 2.5e-3 of (1).
 """
 import numpy as np
 import pytest
 
 import oracle
 from diffusion_transformer_joint_amd import inputs as I
+from oracle.rope import rope_angles
 
 from gpu_helpers import custom, errors, say, to_device
 
@@ -37,13 +41,34 @@ S = I.Segment
 GRAD_REL_L2 = 1.5e-2
 
 
+def _rope_fp16_angles(x, pos, axes):
+    """R(x) with cos and sin rounded to fp16 (RNE), evaluated in fp64."""
+    ang = rope_angles(pos, axes)
+    c = np.cos(ang).astype(np.float16).astype(np.float64)[None, :, None, :]
+    s = np.sin(ang).astype(np.float16).astype(np.float64)[None, :, None, :]
+    out = np.empty_like(x)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def _angle_err(x):
+    """Per-component bound on |R16(x) - R(x)|: (2^-12 + 2^-22)(|x0| + |x1|) of its pair."""
+    p = np.abs(x[..., 0::2]) + np.abs(x[..., 1::2])
+    return (2.0 ** -12 + 2.0 ** -22) * np.repeat(p, 2, axis=-1)
+
+
 def _lse_bounds(q, k, pos, axes, scale):
-    """(lse on bf16-rounded score operands, per-row bound on |lse - exact|)."""
+    """(lse on the kernel's bf16 operands, flip term, per-row bound on |lse - exact|)."""
     c = scale * 1.4426950408889634
     qr = oracle.apply_rope(q, pos, axes) * c
     kr = oracle.apply_rope(k, pos, axes)
     rnd = lambda x: I.bf16_bits_to_f32(I.f32_to_bf16_bits(x.astype(np.float32))).astype(np.float64)
-    qb, kb = rnd(qr), rnd(kr)
+    qb, kb = rnd(_rope_fp16_angles(q, pos, axes) * c), rnd(_rope_fp16_angles(k, pos, axes))
+    eq, ek = _angle_err(q) * c, _angle_err(k)
+    dq = 2.0 ** -9 * (np.abs(qr) + eq) + eq
+    dk = 2.0 ** -9 * (np.abs(kr) + ek) + ek
     B, N, H, _ = q.shape
     lse_b = np.empty((B, H, N))
     flip = np.empty((B, H, N))
@@ -53,8 +78,10 @@ def _lse_bounds(q, k, pos, axes, scale):
             s2 = qb[b, :, h] @ kb[b, :, h].T  # exp2 domain
             m = s2.max(axis=1)
             lse_b[b, h] = (m + np.log2(np.exp2(s2 - m[:, None]).sum(axis=1))) * np.log(2.0)
-            bound[b, h] = (2.0 ** -8 + 2.0 ** -18) * np.log(2.0) * (np.abs(qr[b, :, h]) @ np.abs(kr[b, :, h]).T).max(axis=1)
-            amax = np.abs(qr[b, :, h]).max(axis=1) * np.abs(kr[b, :, h]).max()
+            aq, ak = np.abs(qr[b, :, h]), np.abs(kr[b, :, h])
+            ds = dq[b, :, h] @ ak.T + aq @ dk[b, :, h].T + dq[b, :, h] @ dk[b, :, h].T
+            bound[b, h] = np.log(2.0) * ds.max(axis=1)
+            amax = aq.max(axis=1) * ak.max()
             flip[b, h] = 2.0 ** -8 * np.log(2.0) * amax
     return lse_b, flip, bound
 
