@@ -27,6 +27,7 @@
 namespace flux {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct Fp8Cfg {
@@ -52,11 +53,15 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
   f[3] = hi[1];
 }
 
-// Four floats to e4m3 codes (one dword), round to nearest even.
-__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
+// Four floats divided by 2 to e4m3 codes (one dword), round to nearest even.
+// The gfx950 scaled conversion divides by its scale operand before rounding,
+// so the halving costs no instruction; for every input it gives the codes of
+// v_cvt_pk_fp8_f32 on the halved values (checked bitwise on the GPU).
+__device__ __forceinline__ uint32_t f32x4_half_to_e4m3(float a, float b, float c, float d) {
+  s16x2 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, 2.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, 2.0f, true);
+  return __builtin_bit_cast(uint32_t, w);
 }
 
 // One dword of codes (two pairs) rotated by table entries w0, w1 and halved.
@@ -65,7 +70,7 @@ __device__ __forceinline__ uint32_t rope_dword_e4m3(uint32_t x, uint32_t w0, uin
   e4m3x4_to_f32(x, f);
   rot_pair(f[0], f[1], w0, y[0], y[1]);
   rot_pair(f[2], f[3], w1, y[2], y[3]);
-  return f32x4_to_e4m3(0.5f * y[0], 0.5f * y[1], 0.5f * y[2], 0.5f * y[3]);
+  return f32x4_half_to_e4m3(y[0], y[1], y[2], y[3]);
 }
 
 // The 8 pairs of 16 codes x (dword-packed) rotated by their table entries
@@ -77,15 +82,14 @@ __device__ __forceinline__ u32x4 rope16_e4m3(u32x4 x, const u32x4 (&w)[2]) {
   return y;
 }
 
-// 16 codes to 16 bf16 (exact): two 16-byte halves.
+// 16 codes to 16 bf16 (exact): two 16-byte halves.  One gfx950 conversion
+// per code pair (scale 1).
 __device__ __forceinline__ void e4m3x16_to_bf16(u32x4 x, u32x4* lo, u32x4* hi) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float f[4];
-    e4m3x4_to_f32(x[i], f);
     u32x4& dst = i < 2 ? *lo : *hi;
-    dst[(i & 1) * 2 + 0] = pack_bf16(f[0], f[1]);
-    dst[(i & 1) * 2 + 1] = pack_bf16(f[2], f[3]);
+    dst[(i & 1) * 2 + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[i], 1.0f, false));
+    dst[(i & 1) * 2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[i], 1.0f, true));
   }
 }
 
