@@ -5,15 +5,16 @@
 // GPUs", How it works).  Multi-axis form: head_dim is cut into three slices of
 // widths (d0, d1, d2); pair j of slice a is rotated by pos[n][a] * theta^(-2j/d_a).
 // The per-pair frequencies are computed once per plan on the host in double;
-// here each angle is formed and evaluated in double.
+// here each angle is formed in double.
 //
 // Two storage forms:
 //   packed fp16 (the attention kernels): one dword per pair, cos in the low
-//     half and sin in the high half, each rounded to nearest from double:
-//     4 bytes per pair, error at most 2^-12 in each, a small fraction of the
-//     bf16 rounding that follows the rotation;
+//     half and sin in the high half, rounded to nearest: 4 bytes per pair,
+//     error at most 2^-12 (plus ~1e-7 from the fp32 evaluation) in each, a
+//     small fraction of the bf16 rounding that follows the rotation;
 //   float2 (the tile-mask rule, whose pooled scores decide kept tiles and are
-//     compared with an exact rule): (cos, sin) as fp32.
+//     compared with an exact rule): (cos, sin) evaluated in double, stored
+//     as fp32.
 #include "kernels.h"
 
 namespace flux {
@@ -26,13 +27,19 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ pos, const double*
   const int n = idx / half, p = idx - n * half;
   const int axis = p < p0 ? 0 : (p < p0 + p1 ? 1 : 2);
   const double ang = (double)pos[3 * n + axis] * freq[p];
-  double s, c;
-  sincos(ang, &s, &c);
   if constexpr (PACKED16) {
+    // The angle is reduced to [-pi, pi] in double and evaluated in fp32:
+    // error ~1e-7, far below the fp16 rounding (2^-12) that follows.
+    constexpr double kTwoPi = 6.283185307179586476925286766559;
+    const float r = (float)(ang - kTwoPi * rint(ang * (1.0 / kTwoPi)));
+    float s, c;
+    sincosf(r, &s, &c);
     const uint32_t ch = __builtin_bit_cast(uint16_t, (_Float16)c);
     const uint32_t sh = __builtin_bit_cast(uint16_t, (_Float16)s);
     static_cast<uint32_t*>(table)[idx] = ch | (sh << 16);
   } else {
+    double s, c;
+    sincos(ang, &s, &c);
     static_cast<float2*>(table)[idx] = make_float2((float)c, (float)s);
   }
 }
