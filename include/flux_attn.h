@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   FLUX_ATTN_OK = 0,
   FLUX_ATTN_INVALID_ARGUMENT = 1, /* a pointer, size or shape is wrong */
-  FLUX_ATTN_UNSUPPORTED = 2,      /* valid request this build does not run */
+  FLUX_ATTN_UNSUPPORTED = 2,      /* valid request that the library does not run */
   FLUX_ATTN_DEVICE_ERROR = 3,     /* a HIP runtime call failed */
   FLUX_ATTN_OUT_OF_MEMORY = 4     /* device allocation in create() failed */
 } flux_attn_status;
