@@ -278,7 +278,14 @@ def cpu_baseline(workload, rows_count):
     oracle.joint_rope_attention_rows(q, k, v, inp.pos, w.axes_dim, rows)
     dt = time.perf_counter() - t0
     flops = 4.0 * w.batch * w.heads * len(rows) * w.tokens * w.head_dim
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": round(dt, 2), "gflops": round(flops / dt / 1e9, 1), "cpu": cpu,
             "sample": f"{len(rows)} of {w.tokens} query rows, all {w.heads} heads, full K/V "
                       f"(RoPE of all keys included), {workload}; {dt:.1f} s"}
 
