@@ -20,7 +20,11 @@
  * Conventions where the pages are silent: scale = 1/sqrt(head_dim); RoPE pairs
  * are adjacent elements (2j, 2j+1) inside each axis slice; head_dim is cut into
  * three slices of widths rope_axes_dim[0..2]; pair j of a slice of width d is
- * rotated by pos_axis * theta^(-2j/d); V is not rotated.
+ * rotated by pos_axis * theta^(-2j/d); V is not rotated.  Precision: the
+ * angles are formed in double; the kernels rotate in fp32 with cos and sin
+ * rounded to fp16 (each within 2^-12), round the rotated Q (times scale *
+ * log2 e) and K to bf16 (e4m3 for FP8 plans), accumulate in fp32 and round P
+ * and the output to bf16.
  *
  * Layouts (all row-major, contiguous):
  *   q, k, v, out   [batch][tokens][num_heads][head_dim]
