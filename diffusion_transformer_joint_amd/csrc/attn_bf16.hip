@@ -108,10 +108,14 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
   // Running max folded into the score MFMA: an extra k-step multiplies a
   // column of ones in K by -m in Q, so the accumulator holds c*s - m and
   // p = exp2(acc).  m is kept bf16-representable, so this is exact.  Lanes of
-  // the first half-wave carry k index 0 of the step, the others zeros.
+  // the first half-wave carry k index 0 of the step, the others zeros.  That
+  // product does not depend on the K tile: `fold` (-m in every row of each
+  // query's column) is formed once per change of m and fed as the
+  // accumulator input of the first score MFMA of each block.
   const bf16x8 zero8 = {};
   bf16x8 kone = zero8, qm = zero8;
   if (g == 0) kone[0] = (__bf16)1.0f;
+  f32x16 fold = {};
 
   // ---- staging of K/V tiles: global -> registers -> (K rotated) -> LDS.
   // Each thread owns NPASS (row, 16-byte chunk) slots of a tile, split into two
@@ -256,6 +260,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
   auto set_ref = [&](float m_new) {
     m_ref = m_new;
     if (g == 0) qm[0] = (__bf16)(-m_new);
+    fold = mfma_bf16(kone, qm, (f32x16){});
   };
   auto block_max = [&](const f32x16& s) -> float {
     float mt = s[0];
@@ -404,7 +409,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
     u32x4 fb[NPF];
 #pragma unroll
     for (int j = 0; j < NPF; ++j) fb[j] = ld(j);
-    f32x16 s0 = mfma_bf16(kone, qm, (f32x16){}), s1 = (f32x16){};
+    f32x16 s0, s1;
     u32x4 kr[C::NPASS];
     float b = 0.f;
     __builtin_amdgcn_sched_barrier(0);
@@ -413,10 +418,9 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
       const u32x4 x = fb[j % NPF];
       if constexpr (j + NPF < NL) fb[j % NPF] = ld(j + NPF);
       if constexpr (j < C::KSTEPS) {
-        s0 = mfma_bf16(__builtin_bit_cast(bf16x8, x), qf[j], s0);
-        if constexpr (j == C::KSTEPS - 1) s1 = mfma_bf16(kone, qm, (f32x16){});
+        s0 = mfma_bf16(__builtin_bit_cast(bf16x8, x), qf[j], j == 0 ? fold : s0);
       } else if constexpr (j < NK) {
-        s1 = mfma_bf16(__builtin_bit_cast(bf16x8, x), qf[j - C::KSTEPS], s1);
+        s1 = mfma_bf16(__builtin_bit_cast(bf16x8, x), qf[j - C::KSTEPS], j == C::KSTEPS ? fold : s1);
       } else {
         constexpr int v = j - NK, q4 = v / C::DB, db = v % C::DB;
         o[db] = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, pp[q4]), o[db]);
