@@ -6,8 +6,16 @@
 // on 256 units is 3.19 rounds).  The remedy: run the first F' full rounds as
 // whole tiles and cut each of the remaining L tiles into S key/value ranges, so
 // the last round holds L*S <= C-ish short pieces; the pieces' fp32 partial
-// softmax states are merged exactly afterwards.  (F', S) minimises
-//   F' + ceil(L*S / C) / S + (merge traffic of L*S partials, in rounds).
+// softmax states are merged exactly afterwards.  (F', S) minimises the time
+//   F' (r + o) + ceil(L*S / C) (r / S + o) + (merge traffic of L*S partials)
+// against ceil(T / C) (r + o) without a split, where r is the loop time of a
+// whole tile and o what every work item pays outside its loop.  Both were
+// measured on MI355X with per-workgroup timestamps (bf16, head_dim 128): ~2 us
+// per 64-key step of a 256-row tile, and ~8 us per item for Q staging, the
+// first tile, the epilogue and the change of workgroup on the CU.  With o in
+// the model, a call whose last round is large (4,608 tokens: 432 tiles, 1.69
+// rounds) runs unsplit: cutting 176 tiles into 4 pieces saves less loop time
+// than the 704 items and the merge of their partials cost.
 #include <cmath>
 
 #include "kernels.h"
@@ -18,13 +26,14 @@ Schedule plan_schedule(int tiles, int kv_tiles, int num_cus, int max_pieces, int
   Schedule best{tiles, 0, 1, tiles};
   if (tiles <= 0 || num_cus <= 0) return best;
   const double C = num_cus;
-  double best_cost = std::ceil(tiles / C);
-  // Time of one round of whole tiles and HBM cost of one partial (written and
-  // read back: 256 rows x head_dim fp32 + (m, l)), for the traffic penalty.
-  const double tile_s = 2.5e-6 * head_dim / 128.0;  // one 64-key step of a 256-row tile
+  // Loop time of one whole tile, per-item cost, and HBM cost of one partial
+  // (written and read back: 256 rows x head_dim fp32 + (m, l)).
+  const double tile_s = 2.0e-6 * head_dim / 128.0;  // one 64-key step of a 256-row tile
+  const double item_s = 8.0e-6;
   const double round_s = kv_tiles * tile_s;
   const double piece_bytes = 2.0 * 256.0 * (head_dim * 4.0 + 8.0);
   const double hbm = 6.0e12;
+  double best_cost = std::ceil(tiles / C) * (round_s + item_s);
   const int F = tiles / num_cus;
   for (int Fp = F; Fp >= 0 && Fp >= F - 1; --Fp) {
     const int L = tiles - Fp * num_cus;
@@ -33,7 +42,8 @@ Schedule plan_schedule(int tiles, int kv_tiles, int num_cus, int max_pieces, int
     for (int S = 2; S <= smax; ++S) {
       const long pieces = (long)L * S;
       if (pieces > max_pieces) break;
-      const double cost = Fp + std::ceil(pieces / C) / S + pieces * piece_bytes / hbm / round_s;
+      const double cost =
+          Fp * (round_s + item_s) + std::ceil(pieces / C) * (round_s / S + item_s) + pieces * piece_bytes / hbm;
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
         best = Schedule{Fp * num_cus, L, S, Fp * num_cus + (int)pieces};
