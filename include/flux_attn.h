@@ -102,7 +102,11 @@ int flux_attn_validate_forward(const flux_attn_config* cfg, const void* q, const
  * split-K/V partials; for bf16 plans also the tile-sparse tile means and
  * kept-tile lists, and the backward's row sums and rotated copies of q and k:
  * 2 x batch x max_tokens x num_heads x head_dim bf16).  *out receives the plan, or
- * NULL on error. */
+ * NULL on error.  The environment variable FLUX_ATTN_SCHEDULE, read here,
+ * overrides how the plan's dense bf16 launches split their work: "split" (whole
+ * tiles plus K/V pieces of the last round) or "persistent" (one workgroup per
+ * compute unit over equal slices); unset, the plan chooses by its cost model.
+ * Results agree to rounding under every choice. */
 int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out);
 
 /* Runs joint (or segment-local) RoPE attention asynchronously on hip_stream
