@@ -173,6 +173,16 @@ def test_schedule_fills_last_round():
     assert s["whole_tiles"] == 0 and s["split"] >= 2 and s["grid"] >= 200
 
 
+def test_schedule_keeps_a_large_last_round_whole():
+    # 4,608 tokens x 24 heads: 432 tiles, 1.69 rounds.  Cutting the 176 tiles
+    # of the second round into pieces saves less loop time than the ~8 us
+    # each extra work item and the merge of its partials cost, so the call
+    # runs unsplit; the 8,704-token call (0.19 of a round left) still splits.
+    s = fa.schedule(432, 72, 256, 1024)
+    assert s["split_tiles"] == 0 and s["grid"] == 432
+    assert fa.schedule(816, 136, 256, 1024)["split_tiles"] == 48
+
+
 def test_schedule_respects_piece_cap():
     s = fa.schedule(432, 72, 256, 300)
     assert s["split_tiles"] * s["split"] <= 300 or s["split_tiles"] == 0
