@@ -401,8 +401,10 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
     // Slot plan (slot j follows MFMA j): RoPE of the 4 * NPASS pairs of K(t+1)
     // in every other slot from 0, store of V(t) in slots 1 and 3, loads of
     // V(t+1) in slot 5 and of K(t+2) once its registers are free; P(t) slice q
-    // in the four slots after P(t-1) slice q has been consumed (the last slice
-    // after the stream).
+    // in the four slots after P(t-1) slice q has been consumed.  With D = 128
+    // the last slice is formed early, in slots NK + 2 and NK + 3 (right after
+    // the mask of s1), into spare registers that replace P(t-1) slice 3 after
+    // the stream: the tail after the last MFMA is then short.
     constexpr int NPF = 3;                           // operand reads ahead
     constexpr int ROPE_END = 2 * 4 * C::NPASS;       // slots 0, 2, .., ROPE_END - 2
     constexpr int VST0 = 1, VST1 = 3, LVS = 5, LKS = ROPE_END > NK ? ROPE_END : NK;
@@ -411,6 +413,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
     for (int j = 0; j < NPF; ++j) fb[j] = ld(j);
     f32x16 s0, s1;
     u32x4 kr[C::NPASS];
+    u32x4 pn;  // P(t) slice 3 (D = 128)
     float b = 0.f;
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, NL>([&](auto jc) {
@@ -441,6 +444,13 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
         constexpr int v = j - NK;
         if (LAST && v == 0) mask(kt0, 0, s0);
         if (LAST && v == 2) mask(kt0, 1, s1);
+        if constexpr (D == 128 && (v == 2 || v == 3)) {  // P(t) slice 3, early
+#pragma unroll
+          for (int ee = 0; ee < 2; ++ee) {
+            const int e2 = (v - 2) * 2 + ee;
+            pn[e2] = p_pair(s1[8 + 2 * e2], s1[8 + 2 * e2 + 1], b);
+          }
+        }
         if constexpr (v >= C::DB) {                 // P(t) slice q replaces P(t-1) slice q
           constexpr int q = (v - C::DB) / C::DB, e = (v - C::DB) % C::DB;
           const f32x16& sq = q < 2 ? s0 : s1;
@@ -455,7 +465,10 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
       __builtin_amdgcn_sched_barrier(0);
     });
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) pp[3][e2] = p_pair(s1[8 + 2 * e2], s1[8 + 2 * e2 + 1], b);
+    for (int e2 = 0; e2 < 4; ++e2) {
+      if constexpr (D == 128) pp[3][e2] = pn[e2];
+      else pp[3][e2] = p_pair(s1[8 + 2 * e2], s1[8 + 2 * e2 + 1], b);
+    }
     if (!block_ok(b)) {  // rare: move m up to this tile's max
       const float m_new = fmaxf(m_ref, bf16_round(m_ref + fmaxf(block_max(s0), block_max(s1))));
       rescale_o(__builtin_amdgcn_exp2f(m_ref - m_new));
