@@ -55,14 +55,15 @@ Schedule plan_schedule(int tiles, int kv_tiles, int num_cus, int max_pieces, int
 
 // Dense single-range launches: the split above, or a persistent split in
 // which each of the C workgroups runs an equal slice of the T x kv_tiles tile
-// positions (partials in at most 2 C slots).  Measured on the 8,704-token
-// call: with T >= C (3 heads x 24 would be 816 tiles) the persistent split
-// loses (-9%): a static slice cannot absorb the +-5% spread of per-CU speed
-// that the hardware's dynamic dispatch of split pieces evens out; with T < C
-// (one GPU's 3-head share: 102 tiles) it wins (+10%) over cutting every tile
-// into 5 pieces and running them in two rounds.  So: persistent when T < C
-// and every slice gets at least two positions (mode 0), always where the
-// workspace allows (mode 2), or never (mode 1).
+// positions (partials in at most 2 C slots).  Measured with T >= C (8,704
+// tokens x 24 heads: 816 tiles) the persistent split loses (-8%) although its
+// loop takes no more shader cycles per tile: the chip is power-limited under
+// this loop, and with every CU busy to the end the clock drops (1.57 against
+// 1.67 GHz), which outweighs the better balance.  With T < C (one GPU's 3-head
+// share: 102 tiles) it wins (+10%) over cutting every tile into 5 pieces and
+// running them in two rounds.  So: persistent when T < C and every slice gets
+// at least two positions (mode 0), always where the workspace allows (mode 2),
+// or never (mode 1).
 Schedule plan_schedule_dense(int tiles, int kv_tiles, int num_cus, int max_pieces, int head_dim, int mode) {
   const Schedule base = plan_schedule(tiles, kv_tiles, num_cus, max_pieces, head_dim);
   if (mode == 1 || tiles <= 0 || kv_tiles <= 0 || num_cus < 2 || 2 * num_cus > max_pieces) return base;
