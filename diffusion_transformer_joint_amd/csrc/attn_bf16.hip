@@ -645,7 +645,7 @@ __global__ __launch_bounds__(256) void attn_merge_sk_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
   const size_t tok_stride = (size_t)a.heads * D;
-  *(u32x4*)(a.o + ((size_t)b * a.batch_tokens + row) * tok_stride + (size_t)h * D + d0) = out;
+  *(u32x4*)(a.o + ((size_t)b * a.batch_tokens + a.rng_tok0[0] + row) * tok_stride + (size_t)h * D + d0) = out;
 }
 
 // One thread per (split tile, row, 8 output dims): combines the `split`

@@ -9,24 +9,25 @@
 //   dQ~ = scale dS K~,  dK~ = scale dS^T Q~,  dq = R^T dQ~,  dk = R^T dK~
 // The forward's log-sum-exp (lse) is taken as given; P is recomputed.
 //
-// Four kernels, no atomics:
+// Two launches, no atomics:
 //   attn_bwd_prep_kernel - one pass over the rows: Dr, and bf16 Q~ = R(q),
 //                          K~ = R(k) into workspace, so that the tiles the
-//                          other kernels stream (each is read once per
+//                          streaming workgroups read (each is read once per
 //                          128-row workgroup of the head) need no rotation.
-//   attn_bwd_dkv_kernel  - key-stationary, one instance per gradient: dK
-//                          (S, dP, dS, dK~^T += Q~^T dS) and dV (S, P,
-//                          dV^T += dO^T P).  Splitting them recomputes S once
-//                          more (8 instead of 7 N x N x D products in all) but
-//                          lets each run two waves per SIMD: a fused kernel
-//                          needs both 32-key accumulators and both stationary
-//                          operands in registers, more than half the file.
-//   attn_bwd_dq_kernel   - query-stationary: a wave holds 32 queries (c Q~ and
+//   attn_bwd_kernel      - all three gradients, one workgroup kind per index
+//                          range:
+//     bwd_dkv<true>  (dK)  key-stationary: S, dP, dS, dK~^T += Q~^T dS;
+//     bwd_dq             query-stationary: a wave holds 32 queries (c Q~ and
 //                          dO as B operands); per 64-key tile it forms
-//                          S^T = K~ Q~^T and dP^T = V dO^T (lane = query), then
-//                          dS^T and dQ~^T += K~^T dS^T (K~ through the
-//                          transpose read).
-// The streaming kernels: 4 waves per workgroup (32 rows each, 128 rows), two
+//                          S^T = K~ Q~^T and dP^T = V dO^T (lane = query),
+//                          then dS^T and dQ~^T += K~^T dS^T (K~ through the
+//                          transpose read);
+//     bwd_dkv<false> (dV)  key-stationary: S, P, dV^T += dO^T P.
+//   dK and dV are separate workgroups: that recomputes S once more (8 instead
+//   of 7 N x N x D products in all) but lets each run two waves per SIMD; a
+//   fused body needs both 32-key accumulators and both stationary operands in
+//   registers, more than half the register file.
+// The streaming workgroups: 4 waves per workgroup (32 rows each, 128 rows), two
 // workgroups per CU; the 32x32x16 bf16 MFMA with fp32 accumulation; 64-row
 // tiles stream from global memory straight into double-buffered LDS (buffer
 // loads with the LDS destination, issued one tile ahead, one barrier per

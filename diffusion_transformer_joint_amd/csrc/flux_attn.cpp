@@ -79,7 +79,7 @@ struct flux_attn_plan {
   int num_cus = 0;
   int max_pieces = 0;
   int sched_mode = 0;  // FLUX_ATTN_SCHEDULE at creation: 0 by cost, 1 'split', 2 'persistent'
-  std::vector<hipEvent_t> ev_start, ev_stop;  // kernel timing pairs
+  std::vector<hipEvent_t> ev_start, ev_mid, ev_stop;  // kernel timing: attention | merge
   int timing_used = 0;
 };
 
@@ -90,8 +90,10 @@ uint32_t* rope16(flux_attn_plan* p) { return static_cast<uint32_t*>(p->rope_tabl
 
 void release_timing(flux_attn_plan* p) {
   for (auto e : p->ev_start) (void)hipEventDestroy(e);
+  for (auto e : p->ev_mid) (void)hipEventDestroy(e);
   for (auto e : p->ev_stop) (void)hipEventDestroy(e);
   p->ev_start.clear();
+  p->ev_mid.clear();
   p->ev_stop.clear();
   p->timing_used = 0;
 }
@@ -170,10 +172,18 @@ int flux_attn_validate_config(const flux_attn_config* c) {
   if (!std::isfinite(c->softmax_scale)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "softmax_scale must be finite");
   if (c->dtype != FLUX_ATTN_BF16 && c->dtype != FLUX_ATTN_FP8_E4M3)
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "unknown dtype %d", c->dtype);
-  // Offsets inside one [B][N][H][D] tensor are formed in 64-bit; the token count
-  // must still index a 32-bit grid.
+  // Offsets inside one [B][N][H][D] tensor are formed in 64-bit, but the
+  // kernels read a batch entry's tokens through buffer resources whose range
+  // (num_records) is 32-bit: one batch entry of q, k or v must stay under 4 GiB,
+  // or rows past the wrapped range would read as zeros.
   const double elems = (double)c->batch * c->max_tokens * c->num_heads * c->head_dim;
   if (elems > 9.0e15) return fail(FLUX_ATTN_INVALID_ARGUMENT, "tensor too large");
+  const double entry_bytes = (double)c->max_tokens * c->num_heads * c->head_dim *
+                             (c->dtype == FLUX_ATTN_FP8_E4M3 ? 1.0 : 2.0);
+  if (entry_bytes >= 4294967296.0)
+    return fail(FLUX_ATTN_UNSUPPORTED,
+                "one batch entry of q/k/v is %.0f bytes; the kernels address at most 4 GiB per entry",
+                entry_bytes);
   return ok();
 }
 
@@ -182,11 +192,9 @@ namespace {
 // The forward() checks of everything but the output tensor.
 int validate_inputs(const flux_attn_config* c, const void* q, const void* k, const void* v,
                     const float* qkv_scale, const int32_t* segment_tokens, int32_t num_segments,
-                    const int32_t* pos_ids, int32_t mode, long long* n_out) {
+                    const int32_t* pos_ids, long long* n_out) {
   int st = flux_attn_validate_config(c);
   if (st) return st;
-  if (mode != FLUX_ATTN_JOINT && mode != FLUX_ATTN_SEGMENT_LOCAL)
-    return fail(FLUX_ATTN_INVALID_ARGUMENT, "unknown mode %d", mode);
   if (!segment_tokens) return fail(FLUX_ATTN_INVALID_ARGUMENT, "segment_tokens is NULL");
   if (num_segments < 1 || num_segments > c->max_segments)
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "num_segments = %d outside [1, %d]", num_segments, c->max_segments);
@@ -215,9 +223,9 @@ int validate_inputs(const flux_attn_config* c, const void* q, const void* k, con
 
 int flux_attn_validate_forward(const flux_attn_config* c, const void* q, const void* k, const void* v,
                                const float* qkv_scale, const int32_t* segment_tokens, int32_t num_segments,
-                               const int32_t* pos_ids, const void* out, int32_t mode) {
+                               const int32_t* pos_ids, const void* out) {
   long long n = 0;
-  int st = validate_inputs(c, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, mode, &n);
+  int st = validate_inputs(c, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, &n);
   if (st) return st;
   if (!out) return fail(FLUX_ATTN_INVALID_ARGUMENT, "a tensor pointer is NULL");
   if (!aligned16(out)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "q, k, v and out must be 16-byte aligned");
@@ -339,10 +347,10 @@ int set_ranges(flux::AttnArgs& a, const int* tok0s, const int* lens, int n, int 
 
 int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void* v, const float* qkv_scale,
                  const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
-                 int32_t mode, float* lse, void* hip_stream) {
+                 bool joint, float* lse, void* hip_stream) {
   if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
   const flux_attn_config& c = plan->cfg;
-  int st = flux_attn_validate_forward(&c, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out, mode);
+  int st = flux_attn_validate_forward(&c, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out);
   if (st) return st;
   int n = 0;
   for (int i = 0; i < num_segments; ++i) n += segment_tokens[i];
@@ -363,7 +371,6 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
   // the last round of the long ones; e4m3: one launch per range.  Launches run
   // one after another on the stream and share the plan's partial-state
   // workspace.
-  const bool joint = mode == FLUX_ATTN_JOINT;
   std::vector<int> tok0s, lens;
   {
     int off = 0;
@@ -442,15 +449,20 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
       e = flux::launch_attn_bf16(a, c.head_dim, sch, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "attention launch");
-    // The joint call's timing pair brackets its attention kernel alone; in
-    // segment-local mode it spans all launches (merges between them included).
+    // The joint call's first timing interval brackets its attention kernel
+    // alone; in segment-local mode it spans all launches (merges between them
+    // included).  The second interval is the last merge.
     if (timed && li == n_launch - 1) {
-      e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
+      e = hipEventRecord(plan->ev_mid[plan->timing_used], stream);
       if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-      ++plan->timing_used;
     }
     e = flux::launch_attn_merge(a, c.head_dim, sch, stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  if (timed) {
+    e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    ++plan->timing_used;
   }
   return ok();
 }
@@ -459,8 +471,15 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
 
 int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const void* v, const float* qkv_scale,
                       const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
-                      int32_t mode, void* hip_stream) {
-  return forward_impl(plan, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out, mode, nullptr,
+                      void* hip_stream) {
+  return forward_impl(plan, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out, true, nullptr,
+                      hip_stream);
+}
+
+int flux_attn_forward_segment_local(flux_attn_plan* plan, const void* q, const void* k, const void* v,
+                                    const float* qkv_scale, const int32_t* segment_tokens, int32_t num_segments,
+                                    const int32_t* pos_ids, void* out, void* hip_stream) {
+  return forward_impl(plan, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out, false, nullptr,
                       hip_stream);
 }
 
@@ -470,7 +489,7 @@ int flux_attn_forward_lse(flux_attn_plan* plan, const void* q, const void* k, co
   if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
   if (plan->cfg.dtype != FLUX_ATTN_BF16) return fail(FLUX_ATTN_UNSUPPORTED, "the training forward needs a bf16 plan");
   if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "lse is NULL or misaligned");
-  return forward_impl(plan, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, out, FLUX_ATTN_JOINT, lse,
+  return forward_impl(plan, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, out, true, lse,
                       hip_stream);
 }
 
@@ -480,8 +499,7 @@ int flux_attn_backward(flux_attn_plan* plan, const void* q, const void* k, const
   if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
   const flux_attn_config& c = plan->cfg;
   if (c.dtype != FLUX_ATTN_BF16) return fail(FLUX_ATTN_UNSUPPORTED, "the backward needs a bf16 plan");
-  int st = flux_attn_validate_forward(&c, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, out,
-                                      FLUX_ATTN_JOINT);
+  int st = flux_attn_validate_forward(&c, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, out);
   if (st) return st;
   if (!dout || !lse || !dq || !dk || !dv) return fail(FLUX_ATTN_INVALID_ARGUMENT, "a gradient pointer is NULL");
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
@@ -537,7 +555,8 @@ int flux_attn_backward(flux_attn_plan* plan, const void* q, const void* k, const
   e = flux::launch_attn_bwd(a, c.head_dim, stream);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   if (timed) {
-    e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
+    e = hipEventRecord(plan->ev_mid[plan->timing_used], stream);
+    if (e == hipSuccess) e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     ++plan->timing_used;
   }
@@ -555,9 +574,8 @@ int sparse_common(flux_attn_plan* plan, const void* q, const void* k, const void
   const flux_attn_config& c = plan->cfg;
   if (c.dtype != FLUX_ATTN_BF16) return fail(FLUX_ATTN_UNSUPPORTED, "tile-sparse attention needs a bf16 plan");
   long long nn = 0;
-  int st = out ? flux_attn_validate_forward(&c, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, out,
-                                            FLUX_ATTN_JOINT)
-               : validate_inputs(&c, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, FLUX_ATTN_JOINT, &nn);
+  int st = out ? flux_attn_validate_forward(&c, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, out)
+               : validate_inputs(&c, q, k, v, nullptr, segment_tokens, num_segments, pos_ids, &nn);
   if (st) return st;
   if (!mask) return fail(FLUX_ATTN_INVALID_ARGUMENT, "mask is NULL");
   int n = 0;
@@ -655,12 +673,16 @@ int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k,
   e = flux::launch_attn_bf16(a, c.head_dim, sch, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (timed) {
+    e = hipEventRecord(plan->ev_mid[plan->timing_used], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  e = flux::launch_attn_merge(a, c.head_dim, sch, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  if (timed) {
     e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     ++plan->timing_used;
   }
-  e = flux::launch_attn_merge(a, c.head_dim, sch, stream);
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();
 }
 
@@ -683,25 +705,24 @@ int flux_attn_timing_enable(flux_attn_plan* plan, int32_t capacity) {
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "timing capacity %d outside [0, 4096]", capacity);
   release_timing(plan);
   for (int i = 0; i < capacity; ++i) {
-    hipEvent_t a, b;
-    hipError_t e = hipEventCreate(&a);
-    if (e != hipSuccess) {
-      release_timing(plan);
-      return hip_fail(e, "hipEventCreate");
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    for (int j = 0; j < 3; ++j) {
+      hipError_t e = hipEventCreate(&ev[j]);
+      if (e != hipSuccess) {
+        for (int jj = 0; jj < j; ++jj) (void)hipEventDestroy(ev[jj]);
+        release_timing(plan);
+        return hip_fail(e, "hipEventCreate");
+      }
     }
-    e = hipEventCreate(&b);
-    if (e != hipSuccess) {
-      (void)hipEventDestroy(a);
-      release_timing(plan);
-      return hip_fail(e, "hipEventCreate");
-    }
-    plan->ev_start.push_back(a);
-    plan->ev_stop.push_back(b);
+    plan->ev_start.push_back(ev[0]);
+    plan->ev_mid.push_back(ev[1]);
+    plan->ev_stop.push_back(ev[2]);
   }
   return ok();
 }
 
-int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, int32_t max_count, int32_t* count) {
+int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, float* total_ms, int32_t max_count,
+                          int32_t* count) {
   if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
   if (!count || (max_count > 0 && !attn_ms)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "output pointer is NULL");
   *count = 0;
@@ -711,7 +732,8 @@ int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, int32_t max_coun
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     const int m = n < max_count ? n : max_count;
     for (int i = 0; i < m; ++i) {
-      e = hipEventElapsedTime(&attn_ms[i], plan->ev_start[i], plan->ev_stop[i]);
+      e = hipEventElapsedTime(&attn_ms[i], plan->ev_start[i], plan->ev_mid[i]);
+      if (e == hipSuccess && total_ms) e = hipEventElapsedTime(&total_ms[i], plan->ev_start[i], plan->ev_stop[i]);
       if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
     }
     *count = m;

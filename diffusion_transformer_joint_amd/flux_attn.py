@@ -21,8 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "flux_attn.h")
 
 OK, INVALID_ARGUMENT, UNSUPPORTED, DEVICE_ERROR, OUT_OF_MEMORY = 0, 1, 2, 3, 4
 BF16, FP8_E4M3 = 0, 1
-JOINT, SEGMENT_LOCAL = 0, 1
-_MODES = {"joint": JOINT, "segment_local": SEGMENT_LOCAL}
+_MODES = ("joint", "segment_local")
 
 
 class FluxAttnError(RuntimeError):
@@ -69,9 +68,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     sig = {
         "flux_attn_default_config": ([cp, _i32, _i32, _i32, _i32], ctypes.c_int),
         "flux_attn_validate_config": ([cp], ctypes.c_int),
-        "flux_attn_validate_forward": ([cp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _i32], ctypes.c_int),
+        "flux_attn_validate_forward": ([cp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp], ctypes.c_int),
         "flux_attn_create": ([cp, ctypes.POINTER(_vp)], ctypes.c_int),
-        "flux_attn_forward": ([_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _i32, _vp], ctypes.c_int),
+        "flux_attn_forward": ([_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp], ctypes.c_int),
+        "flux_attn_forward_segment_local": ([_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp], ctypes.c_int),
         "flux_attn_get_config": ([_vp, cp], ctypes.c_int),
         "flux_attn_destroy": ([_vp], ctypes.c_int),
         "flux_attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -79,7 +79,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flux_attn_abi_version": ([], ctypes.c_int),
         "flux_attn_timing_enable": ([_vp, _i32], ctypes.c_int),
         "flux_attn_schedule": ([_i32, _i32, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p], ctypes.c_int),
-        "flux_attn_timing_read": ([_vp, ctypes.POINTER(ctypes.c_float), _i32, _i32p], ctypes.c_int),
+        "flux_attn_timing_read": ([_vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), _i32,
+                                   _i32p], ctypes.c_int),
         "flux_attn_block_mask": ([_vp, _vp, _vp, _i32p, _i32, _vp, ctypes.c_float, _vp, _vp], ctypes.c_int),
         "flux_attn_forward_sparse": ([_vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
         "flux_attn_forward_lse": ([_vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
@@ -143,6 +144,21 @@ def _i32_array(values: Sequence[int]):
     return arr
 
 
+def _device_tensor(name, t, device, shape=None, dtype=None):
+    """Reject a tensor the kernels cannot address: not on ``device``, not
+    contiguous, or of the wrong shape or dtype.  The C side cannot tell a host
+    pointer from a device pointer, so this is the only guard against handing a
+    kernel host memory."""
+    if not t.is_cuda or t.device != device:
+        raise FluxAttnError(INVALID_ARGUMENT, f"{name} must be a tensor on {device} (got {t.device})")
+    if not t.is_contiguous():
+        raise FluxAttnError(INVALID_ARGUMENT, f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise FluxAttnError(INVALID_ARGUMENT, f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise FluxAttnError(INVALID_ARGUMENT, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
 class Plan:
     """A plan for one configuration; owns the library's device workspace."""
 
@@ -166,65 +182,46 @@ class Plan:
 
         q, k, v: [B, N, H, D] contiguous bf16 (or uint8 / float8_e4m3fn codes for an
         FP8 plan); pos_ids: [N, 3] int32; scales: [3, B, H] float32 (FP8 only);
-        out: optional [B, N, H, D] bf16 destination.  Returns out.
+        out: optional [B, N, H, D] bf16 destination.  mode "joint" calls
+        flux_attn_forward, "segment_local" flux_attn_forward_segment_local.
+        Returns out.
         """
         import torch
 
-        if self._handle is None:
-            raise FluxAttnError(INVALID_ARGUMENT, "plan is closed")
-        for name, t in (("q", q), ("k", k), ("v", v), ("pos_ids", pos_ids)):
-            if not t.is_cuda or not t.is_contiguous():
-                raise FluxAttnError(INVALID_ARGUMENT, f"{name} must be a contiguous device tensor")
-        want = (torch.uint8, torch.float8_e4m3fn) if self.fp8 else (torch.bfloat16,)
-        for name, t in (("q", q), ("k", k), ("v", v)):
-            if t.dtype not in want:
-                raise FluxAttnError(INVALID_ARGUMENT, f"{name} has dtype {t.dtype}, expected {want}")
-        if pos_ids.dtype != torch.int32:
-            raise FluxAttnError(INVALID_ARGUMENT, "pos_ids must be int32")
-        n = int(sum(segment_tokens))
+        if mode not in _MODES:
+            raise FluxAttnError(INVALID_ARGUMENT, f"unknown mode {mode!r}")
+        want = (torch.uint8, torch.float8_e4m3fn) if self.fp8 else torch.bfloat16
+        n, shape = self._check_qkv(q, k, v, segment_tokens, pos_ids, want)
         c = self.config
-        shape = (c.batch, n, c.num_heads, c.head_dim)
-        if tuple(q.shape) != shape or tuple(k.shape) != shape or tuple(v.shape) != shape:
-            raise FluxAttnError(INVALID_ARGUMENT, f"q/k/v must have shape {shape}")
-        if tuple(pos_ids.shape) != (n, 3):
-            raise FluxAttnError(INVALID_ARGUMENT, f"pos_ids must have shape {(n, 3)}")
         if out is None:
             out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
-        elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-            raise FluxAttnError(INVALID_ARGUMENT, f"out must be a contiguous bf16 tensor of shape {shape}")
+        else:
+            _device_tensor("out", out, q.device, shape, torch.bfloat16)
         sp = None
         if scales is not None:
-            if tuple(scales.shape) != (3, c.batch, c.num_heads) or scales.dtype != torch.float32 \
-                    or not scales.is_cuda or not scales.is_contiguous():
-                raise FluxAttnError(INVALID_ARGUMENT, "scales must be a contiguous float32 [3, B, H] device tensor")
+            _device_tensor("scales", scales, q.device, (3, c.batch, c.num_heads), torch.float32)
             sp = scales.data_ptr()
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         segs = _i32_array(segment_tokens)
-        check(self._lib.flux_attn_forward(self._handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), sp,
-                                          segs, len(segment_tokens), pos_ids.data_ptr(), out.data_ptr(),
-                                          _MODES[mode], stream.cuda_stream), "forward")
+        fn = self._lib.flux_attn_forward if mode == "joint" else self._lib.flux_attn_forward_segment_local
+        check(fn(self._handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), sp, segs, len(segment_tokens),
+                 pos_ids.data_ptr(), out.data_ptr(), stream.cuda_stream), mode)
         return out
 
-    def _check_qkv(self, q, k, v, segment_tokens, pos_ids):
+    def _check_qkv(self, q, k, v, segment_tokens, pos_ids, want=None):
         import torch
         if self._handle is None:
             raise FluxAttnError(INVALID_ARGUMENT, "plan is closed")
-        for name, t in (("q", q), ("k", k), ("v", v), ("pos_ids", pos_ids)):
-            if not t.is_cuda or not t.is_contiguous():
-                raise FluxAttnError(INVALID_ARGUMENT, f"{name} must be a contiguous device tensor")
-        for name, t in (("q", q), ("k", k), ("v", v)):
-            if t.dtype != torch.bfloat16:
-                raise FluxAttnError(INVALID_ARGUMENT, f"{name} has dtype {t.dtype}, expected bfloat16")
-        if pos_ids.dtype != torch.int32:
-            raise FluxAttnError(INVALID_ARGUMENT, "pos_ids must be int32")
+        want = torch.bfloat16 if want is None else want
         n = int(sum(segment_tokens))
         c = self.config
         shape = (c.batch, n, c.num_heads, c.head_dim)
-        if tuple(q.shape) != shape or tuple(k.shape) != shape or tuple(v.shape) != shape:
-            raise FluxAttnError(INVALID_ARGUMENT, f"q/k/v must have shape {shape}")
-        if tuple(pos_ids.shape) != (n, 3):
-            raise FluxAttnError(INVALID_ARGUMENT, f"pos_ids must have shape {(n, 3)}")
+        if not q.is_cuda:
+            raise FluxAttnError(INVALID_ARGUMENT, f"q must be a device tensor (got {q.device})")
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _device_tensor(name, t, q.device, shape, want)
+        _device_tensor("pos_ids", pos_ids, q.device, (n, 3), torch.int32)
         return n, shape
 
     def mask_shape(self, n_tokens: int) -> tuple:
@@ -239,8 +236,8 @@ class Plan:
         ms = self.mask_shape(n)
         if mask is None:
             mask = torch.empty(ms, dtype=torch.uint8, device=q.device)
-        elif tuple(mask.shape) != ms or mask.dtype != torch.uint8 or not mask.is_contiguous():
-            raise FluxAttnError(INVALID_ARGUMENT, f"mask must be a contiguous uint8 tensor of shape {ms}")
+        else:
+            _device_tensor("mask", mask, q.device, ms, torch.uint8)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         segs = _i32_array(segment_tokens)
@@ -254,12 +251,11 @@ class Plan:
         import torch
         n, shape = self._check_qkv(q, k, v, segment_tokens, pos_ids)
         ms = self.mask_shape(n)
-        if tuple(mask.shape) != ms or mask.dtype != torch.uint8 or not mask.is_cuda or not mask.is_contiguous():
-            raise FluxAttnError(INVALID_ARGUMENT, f"mask must be a contiguous uint8 device tensor of shape {ms}")
+        _device_tensor("mask", mask, q.device, ms, torch.uint8)
         if out is None:
             out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
-        elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-            raise FluxAttnError(INVALID_ARGUMENT, f"out must be a contiguous bf16 tensor of shape {shape}")
+        else:
+            _device_tensor("out", out, q.device, shape, torch.bfloat16)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         segs = _i32_array(segment_tokens)
@@ -275,13 +271,13 @@ class Plan:
         c = self.config
         if out is None:
             out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
-        elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-            raise FluxAttnError(INVALID_ARGUMENT, f"out must be a contiguous bf16 tensor of shape {shape}")
+        else:
+            _device_tensor("out", out, q.device, shape, torch.bfloat16)
         ls = (c.batch, c.num_heads, n)
         if lse is None:
             lse = torch.empty(ls, dtype=torch.float32, device=q.device)
-        elif tuple(lse.shape) != ls or lse.dtype != torch.float32 or not lse.is_contiguous():
-            raise FluxAttnError(INVALID_ARGUMENT, f"lse must be a contiguous float32 tensor of shape {ls}")
+        else:
+            _device_tensor("lse", lse, q.device, ls, torch.float32)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         segs = _i32_array(segment_tokens)
@@ -296,10 +292,8 @@ class Plan:
         n, shape = self._check_qkv(q, k, v, segment_tokens, pos_ids)
         c = self.config
         for name, t in (("out", out), ("dout", dout)):
-            if tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
-                raise FluxAttnError(INVALID_ARGUMENT, f"{name} must be a contiguous bf16 device tensor of shape {shape}")
-        if tuple(lse.shape) != (c.batch, c.num_heads, n) or lse.dtype != torch.float32 or not lse.is_contiguous():
-            raise FluxAttnError(INVALID_ARGUMENT, "lse must be a contiguous float32 [B, H, N] tensor")
+            _device_tensor(name, t, q.device, shape, torch.bfloat16)
+        _device_tensor("lse", lse, q.device, (c.batch, c.num_heads, n), torch.float32)
         dq, dk, dv = (torch.empty(shape, dtype=torch.bfloat16, device=q.device) for _ in range(3))
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
@@ -314,12 +308,17 @@ class Plan:
         """Record the attention kernel's duration for the next ``capacity`` forwards."""
         check(self._lib.flux_attn_timing_enable(self._handle, int(capacity)), "timing_enable")
 
-    def timing_read(self, max_count: int = 4096) -> list:
-        """Durations (ms) of the attention kernels recorded since timing_enable/last read."""
+    def timing_read(self, max_count: int = 4096, with_merge: bool = False):
+        """Durations (ms) of the attention kernels recorded since timing_enable/last read.
+
+        with_merge: also return the durations of attention kernel plus the merge
+        of its split pieces, as a second list."""
         buf = (ctypes.c_float * max_count)()
+        tot = (ctypes.c_float * max_count)()
         n = ctypes.c_int32(0)
-        check(self._lib.flux_attn_timing_read(self._handle, buf, max_count, ctypes.byref(n)), "timing_read")
-        return [buf[i] for i in range(n.value)]
+        check(self._lib.flux_attn_timing_read(self._handle, buf, tot, max_count, ctypes.byref(n)), "timing_read")
+        attn = [buf[i] for i in range(n.value)]
+        return (attn, [tot[i] for i in range(n.value)]) if with_merge else attn
 
     def close(self) -> None:
         if getattr(self, "_handle", None) is not None:

@@ -13,7 +13,7 @@
  *     concatenated and attend jointly in the joint blocks;
  *   - "FLUX.3 Image Klein Brings 2-Second AI Image Generation to Diffusers",
  *     Summary: five separate-stream blocks before 28 joint blocks (the
- *     segment-local mode below is the separate-stream attention);
+ *     segment-local entry point below is the separate-stream attention);
  *   - "Optimizing FLUX 3 Image Klein inference on NVIDIA Blackwell GPUs",
  *     "How it works": rotary position embeddings, and attention with query,
  *     key and value in FP8.
@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FLUX_ATTN_ABI_VERSION 1
+#define FLUX_ATTN_ABI_VERSION 2
 
 typedef enum {
   FLUX_ATTN_OK = 0,
@@ -60,16 +60,15 @@ typedef enum {
   FLUX_ATTN_FP8_E4M3 = 1  /* q, k, v are OCP e4m3 ("e4m3fn") codes + per-head scales */
 } flux_attn_dtype;
 
-typedef enum {
-  FLUX_ATTN_JOINT = 0,         /* every token attends to every token */
-  FLUX_ATTN_SEGMENT_LOCAL = 1  /* tokens attend only inside their own segment */
-} flux_attn_mode;
-
 typedef struct {
   int32_t batch;            /* >= 1 */
   int32_t num_heads;        /* >= 1 */
   int32_t head_dim;         /* 64 or 128 */
-  int32_t max_tokens;       /* capacity: largest token count forward() will see */
+  int32_t max_tokens;       /* capacity: largest token count forward() will see;
+                               one batch entry of q, k or v (max_tokens x num_heads
+                               x head_dim elements) must stay under 4 GiB
+                               (FLUX_ATTN_UNSUPPORTED otherwise): the kernels
+                               address it through 32-bit buffer ranges */
   int32_t max_segments;     /* capacity of the segment list, >= 1 */
   int32_t rope_axes_dim[3]; /* even, multiples of 8, sum == head_dim */
   float rope_theta;         /* > 0, e.g. 10000 */
@@ -88,14 +87,15 @@ int flux_attn_default_config(flux_attn_config* cfg, int32_t batch, int32_t num_h
 /* Checks a configuration without touching a device.  Host only. */
 int flux_attn_validate_config(const flux_attn_config* cfg);
 
-/* Checks the host-side arguments of a forward call against cfg without touching
- * a device: segment list (each >= 0, sum N with 1 <= N <= max_tokens, count
- * <= max_segments), non-null and 16-byte aligned tensors, out not overlapping
- * q/k/v (by address range), scales present iff FP8, mode known.  Host only. */
+/* Checks the host-side arguments of a forward call (joint or segment-local:
+ * both take the same arguments) against cfg without touching a device: segment
+ * list (each >= 0, sum N with 1 <= N <= max_tokens, count <= max_segments),
+ * non-null and 16-byte aligned tensors, out not overlapping q/k/v (by address
+ * range), scales present iff FP8.  Host only. */
 int flux_attn_validate_forward(const flux_attn_config* cfg, const void* q, const void* k,
                                const void* v, const float* qkv_scale,
                                const int32_t* segment_tokens, int32_t num_segments,
-                               const int32_t* pos_ids, const void* out, int32_t mode);
+                               const int32_t* pos_ids, const void* out);
 
 /* Creates a plan on the current HIP device: validates cfg and allocates the
  * plan's device workspace once (RoPE table of max_tokens x head_dim/2 x 8 bytes,
@@ -109,24 +109,30 @@ int flux_attn_validate_forward(const flux_attn_config* cfg, const void* q, const
  * Results agree to rounding under every choice. */
 int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out);
 
-/* Runs joint (or segment-local) RoPE attention asynchronously on hip_stream
- * (a hipStream_t; NULL = the null stream).  q, k, v, out, pos_ids and
- * qkv_scale are device pointers owned by the caller and must stay valid until
- * the stream has passed this work; segment_tokens is a host array read before
- * the call returns.  N = sum(segment_tokens).  out is fully overwritten.
- * mode FLUX_ATTN_JOINT: every token attends to all N tokens (the joint
- * blocks).  mode FLUX_ATTN_SEGMENT_LOCAL: a token of segment s attends only to
- * the tokens of segment s, i.e. the formula above with j restricted to the
- * segment ("FLUX.3 Image Klein Brings 2-Second AI Image Generation to
- * Diffusers", Summary: the separate-stream blocks before the joint ones); the
- * RoPE angles still come from the tokens' own position ids, and empty
- * segments are skipped.  A plan runs one forward at a time (its workspace is
- * shared between calls and between the segments of one call); separate plans
- * are independent.  Returns after launching. */
+/* Runs joint RoPE attention asynchronously on hip_stream (a hipStream_t; NULL
+ * = the null stream): every token attends to all N tokens of the concatenated
+ * sequence (the joint blocks).  q, k, v, out, pos_ids and qkv_scale are
+ * device pointers owned by the caller and must stay valid until the stream
+ * has passed this work; segment_tokens is a host array read before the call
+ * returns.  N = sum(segment_tokens); the segment counts define N and are
+ * validated, they do not change the arithmetic.  out is fully overwritten.
+ * A plan runs one forward at a time (its workspace is shared between calls);
+ * separate plans are independent.  Returns after launching. */
 int flux_attn_forward(flux_attn_plan* plan, const void* q, const void* k, const void* v,
                       const float* qkv_scale, const int32_t* segment_tokens,
                       int32_t num_segments, const int32_t* pos_ids, void* out,
-                      int32_t mode, void* hip_stream);
+                      void* hip_stream);
+
+/* Segment-local attention, same arguments and rules as flux_attn_forward: a
+ * token of segment s attends only to the tokens of segment s, i.e. the formula
+ * above with j restricted to the segment ("FLUX.3 Image Klein Brings 2-Second
+ * AI Image Generation to Diffusers", Summary: the separate-stream blocks before
+ * the joint ones).  The RoPE angles still come from the tokens' own position
+ * ids, and empty segments are skipped. */
+int flux_attn_forward_segment_local(flux_attn_plan* plan, const void* q, const void* k, const void* v,
+                                    const float* qkv_scale, const int32_t* segment_tokens,
+                                    int32_t num_segments, const int32_t* pos_ids, void* out,
+                                    void* hip_stream);
 
 /* Training: forward with the per-row log-sum-exp, and the backward.  The
  * attention backward is the adjacent training workload (LoRA fine-tuning of
@@ -187,17 +193,20 @@ int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k,
                              const uint8_t* mask, void* out, void* hip_stream);
 
 /* Kernel timing.  flux_attn_timing_enable(plan, capacity) with capacity > 0
- * creates capacity pairs of HIP events (capacity <= 4096); every following
- * forward() records one pair around its attention kernel (none once all pairs
- * are used), on the stream that kernel runs on.  In segment-local mode the
- * pair spans the attention kernels of all segments (the small merge kernels
- * between them included).  capacity = 0 releases them.
- * flux_attn_timing_read() waits for the last recorded pair, writes the
- * durations in milliseconds of up to max_count recorded launches to
- * attn_ms[0..*count-1] (host array) and starts over.  The caller must not
- * read while another thread runs forward() on the plan. */
+ * creates capacity triples of HIP events (capacity <= 4096); every following
+ * forward call records one triple (none once all are used), on the stream its
+ * kernels run on: before the attention kernel, after it, and after the exact
+ * merge of its split pieces (if any).  For segment-local calls the first two
+ * span the attention kernels of all segments (the small merge kernels between
+ * them included).  capacity = 0 releases them.
+ * flux_attn_timing_read() waits for the last recorded triple, writes the
+ * durations in milliseconds of up to max_count recorded calls to host arrays:
+ * attn_ms[i] (attention kernel) and, if total_ms is not NULL, total_ms[i]
+ * (attention kernel plus merge), then starts over.  The caller must not read
+ * while another thread runs forward calls on the plan. */
 int flux_attn_timing_enable(flux_attn_plan* plan, int32_t capacity);
-int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, int32_t max_count, int32_t* count);
+int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, float* total_ms, int32_t max_count,
+                          int32_t* count);
 
 /* Work split chosen by forward() for a launch (host only, no device call).
  * The kernel runs one 256-row query tile of one (batch, head) per workgroup,

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.flux_attn_abi_version() == 1
+    assert lib.flux_attn_abi_version() == 2
     assert lib.flux_attn_status_string(0) == b"ok"
     assert lib.flux_attn_status_string(1) == b"invalid argument"
     assert lib.flux_attn_status_string(99) == b"unknown status"
@@ -63,22 +63,21 @@ A = 1 << 40
 Q, K, V, O, POS, SC = A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A
 
 
-def vf(lib, cfg, segs, q=Q, k=K, v=V, sc=None, pos=POS, out=O, mode=fa.JOINT, nseg=None):
+def vf(lib, cfg, segs, q=Q, k=K, v=V, sc=None, pos=POS, out=O, nseg=None):
     arr = fa._i32_array(segs) if segs is not None else None
     return lib.flux_attn_validate_forward(ctypes.byref(cfg), q, k, v, sc, arr,
-                                          len(segs) if nseg is None else nseg, pos, out, mode)
+                                          len(segs) if nseg is None else nseg, pos, out)
 
 
 def test_validate_forward_ok(lib):
     cfg = fa.default_config(1, 24, 128, 8704)
     assert vf(lib, cfg, [512, 4096, 4096]) == fa.OK
-    assert vf(lib, cfg, [512, 4096, 4096], mode=fa.SEGMENT_LOCAL) == fa.OK
     assert vf(lib, cfg, [0, 7, 0]) == fa.OK
 
 
 @pytest.mark.parametrize("case", [
     "too_many_tokens", "zero_tokens", "negative_segment", "too_many_segments", "null_q", "null_out",
-    "null_pos", "unaligned_q", "unaligned_pos", "scale_on_bf16", "overlap", "bad_mode", "null_segments",
+    "null_pos", "unaligned_q", "unaligned_pos", "scale_on_bf16", "overlap", "null_segments",
 ])
 def test_validate_forward_errors(lib, case):
     cfg = fa.default_config(1, 24, 128, 8704)
@@ -106,10 +105,8 @@ def test_validate_forward_errors(lib, case):
         kw["sc"] = SC
     elif case == "overlap":
         kw["out"] = Q + 4096
-    elif case == "bad_mode":
-        kw["mode"] = 5
     elif case == "null_segments":
-        assert lib.flux_attn_validate_forward(ctypes.byref(cfg), Q, K, V, None, None, 3, POS, O, 0) \
+        assert lib.flux_attn_validate_forward(ctypes.byref(cfg), Q, K, V, None, None, 3, POS, O) \
             == fa.INVALID_ARGUMENT
         return
     assert vf(lib, cfg, segs, **kw) == fa.INVALID_ARGUMENT
@@ -126,11 +123,34 @@ def test_plan_handles_rejected_without_dereference(lib):
     assert lib.flux_attn_destroy(None) == fa.OK
     assert lib.flux_attn_destroy(0x1234560) == fa.INVALID_ARGUMENT
     segs = fa._i32_array([80])
-    assert lib.flux_attn_forward(None, Q, K, V, None, segs, 1, POS, O, 0, None) == fa.INVALID_ARGUMENT
-    assert lib.flux_attn_forward(0x1234560, Q, K, V, None, segs, 1, POS, O, 0, None) == fa.INVALID_ARGUMENT
+    for fn in (lib.flux_attn_forward, lib.flux_attn_forward_segment_local):
+        assert fn(None, Q, K, V, None, segs, 1, POS, O, None) == fa.INVALID_ARGUMENT
+        assert fn(0x1234560, Q, K, V, None, segs, 1, POS, O, None) == fa.INVALID_ARGUMENT
     cfg = fa.Config()
     assert lib.flux_attn_get_config(None, ctypes.byref(cfg)) == fa.INVALID_ARGUMENT
     assert lib.flux_attn_create(None, None) == fa.INVALID_ARGUMENT
+
+
+def test_batch_entry_over_4gib_is_unsupported(lib):
+    # the kernels address one batch entry of q/k/v through 32-bit buffer ranges
+    cfg = fa.default_config(1, 24, 128, 699050)           # 699,050 x 3,072 x 2 B < 4 GiB
+    assert lib.flux_attn_validate_config(ctypes.byref(cfg)) == fa.OK
+    cfg = fa.default_config(1, 24, 128, 699051)           # 699,051 x 3,072 x 2 B >= 4 GiB
+    assert lib.flux_attn_validate_config(ctypes.byref(cfg)) == fa.UNSUPPORTED
+    assert "4 GiB" in fa.last_error()
+    cfg = fa.default_config(1, 24, 128, 699051, dtype="fp8")  # 1 B per e4m3 code: fits
+    assert lib.flux_attn_validate_config(ctypes.byref(cfg)) == fa.OK
+    cfg = fa.default_config(4, 24, 128, 600000)           # the limit is per batch entry
+    assert lib.flux_attn_validate_config(ctypes.byref(cfg)) == fa.OK
+
+
+def test_wrapper_rejects_host_tensors():
+    # the C side cannot tell host from device pointers; the binding refuses
+    # anything that is not a device tensor before any call
+    import torch
+    x = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FluxAttnError, match="must be a tensor on"):
+        fa._device_tensor("out", x, torch.device("cuda:0"))
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -3,10 +3,12 @@
 With the persistent split, one workgroup per compute unit runs an equal slice
 of all (query tile, 64-key tile) positions, storing partial softmax states for
 the tiles its slice cuts, and a merge kernel combines them.  The library picks
-it by cost (the 4,608-token workload uses it); FLUX_ATTN_SCHEDULE=persistent
-forces it at plan creation, which these tests use to cover small, ragged,
-batched and D = 64 launches (including slices of a single position and empty
-slices) against the oracle.
+it by cost where a launch has fewer query tiles than compute units (one GPU's
+3-head share of the 8,704-token call: 102 tiles); the 4,608- and 8,704-token
+calls over all 24 heads run the whole-tile schedule (unsplit and split,
+respectively).  FLUX_ATTN_SCHEDULE=persistent forces it at plan creation,
+which these tests use to cover small, ragged, batched and D = 64 launches
+(including slices of a single position and empty slices) against the oracle.
 """
 import numpy as np
 import pytest

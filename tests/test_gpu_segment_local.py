@@ -93,3 +93,50 @@ def test_segment_local_many_segments():
     finally:
         plan.close()
     assert_close(got, ref_full(inp, mode="segment_local"), BF16_TOL, "seg_many")
+
+
+def test_segment_local_last_launch_persistent_at_offset(monkeypatch):
+    # 17 non-empty segments: the first launch takes the 16 longest, the second
+    # holds only the shortest (100 tokens), which starts at token 600, not 0.
+    # A single-range launch may take the persistent split; forcing it makes
+    # the merge of the cut tile write that segment's rows at their offset.
+    from diffusion_transformer_joint_amd.flux_attn import Plan
+    monkeypatch.setenv("FLUX_ATTN_SCHEDULE", "persistent")
+    lens = [300, 300, 100] + [130 + 10 * i for i in range(14)]
+    segs = [S("text", n) for n in lens]
+    inp = I.make_inputs(custom("seg_tail", 2, 128, segs, sigma=1.0))
+    w = inp.workload
+    plan = Plan(w.batch, w.heads, w.head_dim, w.tokens, max_segments=len(lens))
+    try:
+        got = out_fp64(run_hip(inp, plan=plan, mode="segment_local"))
+    finally:
+        plan.close()
+    assert_close(got, ref_full(inp, mode="segment_local"), BF16_TOL, "seg_tail (persistent, offset 600)")
+
+
+def test_host_tensors_rejected_before_launch():
+    # out, lse and mask on the host: the binding raises before any kernel runs
+    import torch
+    from diffusion_transformer_joint_amd.flux_attn import FluxAttnError, Plan
+    from gpu_helpers import to_device
+    inp = I.make_inputs(custom("hostout", 2, 128, [S("text", 70)]))
+    w = inp.workload
+    q, k, v, pos, _ = to_device(inp)
+    shape = (w.batch, w.tokens, w.heads, w.head_dim)
+    with Plan(w.batch, w.heads, w.head_dim, w.tokens) as plan:
+        for mode in ("joint", "segment_local"):
+            with pytest.raises(FluxAttnError):
+                plan.forward(q, k, v, inp.segment_tokens, pos, out=torch.empty(shape, dtype=torch.bfloat16),
+                             mode=mode)
+        with pytest.raises(FluxAttnError):
+            plan.forward_lse(q, k, v, inp.segment_tokens, pos,
+                             lse=torch.empty((w.batch, w.heads, w.tokens), dtype=torch.float32))
+        with pytest.raises(FluxAttnError):
+            plan.block_mask(q, k, inp.segment_tokens, pos, 0.1,
+                            mask=torch.empty(plan.mask_shape(w.tokens), dtype=torch.uint8))
+        with pytest.raises(FluxAttnError):
+            plan.forward_sparse(q, k, v, inp.segment_tokens, pos,
+                                torch.ones(plan.mask_shape(w.tokens), dtype=torch.uint8))
+        with pytest.raises(FluxAttnError):
+            plan.forward(q.cpu(), k, v, inp.segment_tokens, pos)
+        torch.cuda.synchronize()

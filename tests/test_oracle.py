@@ -291,6 +291,42 @@ def test_e4m3_all_codes_vs_torch():
     np.testing.assert_array_equal(ref[ok], oracle.e4m3_table()[ok])
 
 
+def _bf16_from_format(bits):
+    """bfloat16 decoded from its format definition (1 sign bit, 8 exponent bits
+    with bias 127, 7 fraction bits; exponent 0 holds subnormals f/128 * 2^-126,
+    exponent 255 holds infinities and NaNs): an independent route from the
+    oracle's bit shift."""
+    b = np.asarray(bits, dtype=np.int64)
+    sign = np.where(b & 0x8000, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    f = (b & 0x7F).astype(np.float64)
+    val = np.where(e == 0, (f / 128.0) * 2.0 ** -126, (1.0 + f / 128.0) * np.exp2(e.astype(np.float64) - 127.0))
+    val = np.where(e == 0xFF, np.where(f == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+def test_bf16_widening_all_patterns():
+    # every one of the 65,536 bfloat16 bit patterns: the oracle's widening must
+    # give the format's value exactly (torch's bfloat16 -> float64 cast and the
+    # format definition decoded by hand), NaN exactly where the format has NaN
+    import torch
+    from oracle.inputs_fp64 import bf16_to_fp64
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = bf16_to_fp64(bits)
+    assert got.dtype == np.float64 and got.shape == (65536,)
+    via_torch = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    by_hand = _bf16_from_format(bits)
+    for ref in (via_torch, by_hand):
+        np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+        ok = ~np.isnan(ref)
+        np.testing.assert_array_equal(got[ok], ref[ok])
+        np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))   # -0.0 stays -0.0
+    assert np.isnan(got).sum() == 2 * 127            # exponent 255 with a nonzero fraction
+    # shapes are kept (the oracle widens [B, N, H, D] tensors)
+    x = bits[:24].reshape(1, 2, 3, 4)
+    np.testing.assert_array_equal(bf16_to_fp64(x), got[:24].reshape(1, 2, 3, 4))
+
+
 def test_e4m3_positive_codes_monotone():
     tab = oracle.e4m3_table()[:127]
     assert np.all(np.diff(tab) > 0)
