@@ -64,7 +64,7 @@ struct flux_attn_plan {
   // (cos, sin) for the attention kernels, or fp32 pairs for the tile-mask
   // rule (the allocation is sized for the latter).
   void* rope_table = nullptr;
-  double* freq = nullptr;        // [head_dim/2]
+  flux::RopeFreq freq{};         // per-pair frequencies (host; kernel argument)
   float* part_o = nullptr;       // split-K/V partials: [max_pieces][256][head_dim]
   float2* part_ml = nullptr;     // [max_pieces][256]
   // tile-sparse workspace (bf16 plans): tile means, kept-tile lists
@@ -237,6 +237,22 @@ int flux_attn_validate_forward(const flux_attn_config* c, const void* q, const v
   return ok();
 }
 
+namespace {
+
+// theta^(-2j/d_a) for pair j of axis slice a, in double.
+flux::RopeFreq rope_freq(const flux_attn_config& c) {
+  flux::RopeFreq f{};
+  int j0 = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int d = c.rope_axes_dim[a];
+    for (int j = 0; j < d / 2; ++j) f.f[j0 + j] = std::pow((double)c.rope_theta, -2.0 * j / d);
+    j0 += d / 2;
+  }
+  return f;
+}
+
+}  // namespace
+
 int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
   if (!out) return fail(FLUX_ATTN_INVALID_ARGUMENT, "out is NULL");
   *out = nullptr;
@@ -251,13 +267,7 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     return hip_fail(e, "hipGetDevice");
   }
   const int half = cfg->head_dim / 2;
-  std::vector<double> freq(half);
-  int j0 = 0;
-  for (int a = 0; a < 3; ++a) {
-    const int d = cfg->rope_axes_dim[a];
-    for (int j = 0; j < d / 2; ++j) freq[j0 + j] = std::pow((double)cfg->rope_theta, -2.0 * j / d);
-    j0 += d / 2;
-  }
+  p->freq = rope_freq(*cfg);
   e = hipDeviceGetAttribute(&p->num_cus, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e != hipSuccess) {
     delete p;
@@ -278,8 +288,6 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
     p->max_pieces = (int)(cap < most ? cap : most);
   }
   e = hipMalloc(&p->rope_table, (size_t)cfg->max_tokens * half * sizeof(float2));
-  if (e == hipSuccess) e = hipMalloc(&p->freq, half * sizeof(double));
-  if (e == hipSuccess) e = hipMemcpy(p->freq, freq.data(), half * sizeof(double), hipMemcpyHostToDevice);
   if (e == hipSuccess && p->max_pieces > 0)
     e = hipMalloc(&p->part_o, (size_t)p->max_pieces * 256 * cfg->head_dim * sizeof(float));
   if (e == hipSuccess && p->max_pieces > 0)
@@ -299,7 +307,6 @@ int flux_attn_create(const flux_attn_config* cfg, flux_attn_plan** out) {
   }
   if (e != hipSuccess) {
     (void)hipFree(p->rope_table);
-    (void)hipFree(p->freq);
     (void)hipFree(p->part_o);
     (void)hipFree(p->part_ml);
     (void)hipFree(p->qbar);
@@ -345,23 +352,32 @@ int set_ranges(flux::AttnArgs& a, const int* tok0s, const int* lens, int n, int 
   return tiles;
 }
 
-int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void* v, const float* qkv_scale,
-                 const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
-                 bool joint, float* lse, void* hip_stream) {
-  if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
-  const flux_attn_config& c = plan->cfg;
-  int st = flux_attn_validate_forward(&c, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out);
-  if (st) return st;
+// Device memory and policy one forward call works with.
+struct FwdWorkspace {
+  uint32_t* rope;     // packed fp16 RoPE table, at least N x D/2 entries
+  float* part_o;      // split partials: [max_pieces][256][D]
+  float2* part_ml;    // [max_pieces][256]
+  int max_pieces;
+  int num_cus;
+  int sched_mode;     // 0 by cost, 1 never persistent, 2 persistent where possible
+};
+
+// Optional HIP events bracketing the call: before the attention kernel, after
+// it (before the last merge), and at the end.
+struct FwdEvents {
+  hipEvent_t start, mid, stop;
+};
+
+// The launches of one validated forward call: RoPE table, then the attention
+// kernel(s) and their merges, on `stream`.
+int launch_forward(const flux_attn_config& c, const flux::RopeFreq& freq, const FwdWorkspace& ws, const void* q,
+                   const void* k, const void* v, const float* qkv_scale, const int32_t* segment_tokens,
+                   int32_t num_segments, const int32_t* pos_ids, void* out, bool joint, float* lse,
+                   hipStream_t stream, const FwdEvents* ev) {
   int n = 0;
   for (int i = 0; i < num_segments; ++i) n += segment_tokens[i];
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev != plan->device)
-    return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan was created on device %d, current device is %d", plan->device, dev);
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  e = flux::launch_rope_table(pos_ids, plan->freq, rope16(plan), n, c.head_dim, c.rope_axes_dim[0],
-                              c.rope_axes_dim[1], stream);
+  hipError_t e = flux::launch_rope_table(pos_ids, freq, ws.rope, n, c.head_dim, c.rope_axes_dim[0],
+                                         c.rope_axes_dim[1], stream);
   if (e != hipSuccess) return hip_fail(e, "rope table launch");
   const float scale = c.softmax_scale > 0.0f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
   const float log2e = 1.4426950408889634f;
@@ -369,8 +385,7 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
   // segment on its own (segment-local).  bf16: one attention launch (+ merge)
   // covers up to kMaxRanges ranges, longest first, so that short segments fill
   // the last round of the long ones; e4m3: one launch per range.  Launches run
-  // one after another on the stream and share the plan's partial-state
-  // workspace.
+  // one after another on the stream and share the partial-state workspace.
   std::vector<int> tok0s, lens;
   {
     int off = 0;
@@ -389,9 +404,8 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
   if (!fp8) std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return lens[x] > lens[y]; });
   const int per_launch = fp8 ? 1 : flux::AttnArgs::kMaxRanges;
   const int n_launch = ((int)order.size() + per_launch - 1) / per_launch;
-  const bool timed = plan->timing_used < (int)plan->ev_start.size();
-  if (timed) {
-    e = hipEventRecord(plan->ev_start[plan->timing_used], stream);
+  if (ev) {
+    e = hipEventRecord(ev->start, stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   const size_t tok = (size_t)c.num_heads * c.head_dim;  // elements per token
@@ -408,15 +422,15 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
     const int tiles = set_ranges(a, gt, gl, r1 - r0, c.batch, c.num_heads);
     const flux::Schedule sch =
         (!fp8 && r1 - r0 == 1)
-            ? flux::plan_schedule_dense(tiles, (max_len + 63) / 64, plan->num_cus, plan->max_pieces, c.head_dim,
-                                        plan->sched_mode)
-            : flux::plan_schedule(tiles, (max_len + 63) / 64, plan->num_cus, plan->max_pieces, c.head_dim);
+            ? flux::plan_schedule_dense(tiles, (max_len + 63) / 64, ws.num_cus, ws.max_pieces, c.head_dim,
+                                        ws.sched_mode)
+            : flux::plan_schedule(tiles, (max_len + 63) / 64, ws.num_cus, ws.max_pieces, c.head_dim);
     a.batch_tokens = n;
     a.heads = c.num_heads;
     a.batch = c.batch;
     a.c = scale * log2e;
-    a.part_o = plan->part_o;
-    a.part_ml = plan->part_ml;
+    a.part_o = ws.part_o;
+    a.part_ml = ws.part_ml;
     a.lse = lse;
     if (fp8) {
       const size_t off = (size_t)gt[0];
@@ -426,7 +440,7 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
       f.v = static_cast<const uint8_t*>(v) + off * tok;
       f.scales = qkv_scale;
       f.o = static_cast<uint16_t*>(out) + off * tok;
-      f.rope = rope16(plan) + off * (c.head_dim / 2);
+      f.rope = ws.rope + off * (c.head_dim / 2);
       f.n_tokens = gl[0];
       f.batch_tokens = n;
       f.heads = c.num_heads;
@@ -445,25 +459,51 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
       a.k = static_cast<const uint16_t*>(k);
       a.v = static_cast<const uint16_t*>(v);
       a.o = static_cast<uint16_t*>(out);
-      a.rope = rope16(plan);
+      a.rope = ws.rope;
       e = flux::launch_attn_bf16(a, c.head_dim, sch, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     // The joint call's first timing interval brackets its attention kernel
     // alone; in segment-local mode it spans all launches (merges between them
     // included).  The second interval is the last merge.
-    if (timed && li == n_launch - 1) {
-      e = hipEventRecord(plan->ev_mid[plan->timing_used], stream);
+    if (ev && li == n_launch - 1) {
+      e = hipEventRecord(ev->mid, stream);
       if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
     e = flux::launch_attn_merge(a, c.head_dim, sch, stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
-  if (timed) {
-    e = hipEventRecord(plan->ev_stop[plan->timing_used], stream);
+  if (ev) {
+    e = hipEventRecord(ev->stop, stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    ++plan->timing_used;
   }
+  return ok();
+}
+
+int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void* v, const float* qkv_scale,
+                 const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids, void* out,
+                 bool joint, float* lse, void* hip_stream) {
+  if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
+  const flux_attn_config& c = plan->cfg;
+  int st = flux_attn_validate_forward(&c, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out);
+  if (st) return st;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan was created on device %d, current device is %d", plan->device, dev);
+  const FwdWorkspace ws{rope16(plan), plan->part_o, plan->part_ml, plan->max_pieces, plan->num_cus,
+                        plan->sched_mode};
+  const bool timed = plan->timing_used < (int)plan->ev_start.size();
+  FwdEvents ev{};
+  if (timed) {
+    const int i = plan->timing_used;
+    ev = FwdEvents{plan->ev_start[i], plan->ev_mid[i], plan->ev_stop[i]};
+  }
+  st = launch_forward(c, plan->freq, ws, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out, joint,
+                      lse, static_cast<hipStream_t>(hip_stream), timed ? &ev : nullptr);
+  if (st) return st;
+  if (timed) ++plan->timing_used;
   return ok();
 }
 
@@ -760,10 +800,8 @@ int flux_attn_destroy(flux_attn_plan* plan) {
   (void)hipFree(plan->rq);
   (void)hipFree(plan->rk);
   hipError_t e1 = hipFree(plan->rope_table);
-  hipError_t e2 = hipFree(plan->freq);
   delete plan;
   if (e1 != hipSuccess) return hip_fail(e1, "hipFree");
-  if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
   return ok();
 }
 

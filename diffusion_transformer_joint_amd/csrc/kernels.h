@@ -85,12 +85,18 @@ struct Fp8Args {
   float2* part_ml;
 };
 
+// Per-pair rotary frequencies theta^(-2j/d_a), computed on the host in double
+// and passed to the table kernel by value (no device copy).
+struct RopeFreq {
+  double f[64];  // head_dim / 2 <= 64 pairs
+};
+
 // (cos, sin) of pos[n][axis(p)] * freq[p] for every token n and pair p, as
 // packed fp16 (cos in the low half).
-hipError_t launch_rope_table(const int32_t* pos, const double* freq, uint32_t* table, int n_tokens,
+hipError_t launch_rope_table(const int32_t* pos, const RopeFreq& freq, uint32_t* table, int n_tokens,
                              int head_dim, int d0, int d1, hipStream_t stream);
 // The same angles as fp32 (cos, sin) pairs, for the tile-mask rule.
-hipError_t launch_rope_table_f32(const int32_t* pos, const double* freq, float2* table, int n_tokens,
+hipError_t launch_rope_table_f32(const int32_t* pos, const RopeFreq& freq, float2* table, int n_tokens,
                                  int head_dim, int d0, int d1, hipStream_t stream);
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream);

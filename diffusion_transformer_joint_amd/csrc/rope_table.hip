@@ -4,8 +4,8 @@
 // transformer ("Optimizing FLUX 3 Image Klein inference on NVIDIA Blackwell
 // GPUs", How it works).  Multi-axis form: head_dim is cut into three slices of
 // widths (d0, d1, d2); pair j of slice a is rotated by pos[n][a] * theta^(-2j/d_a).
-// The per-pair frequencies are computed once per plan on the host in double;
-// here each angle is formed in double.
+// The per-pair frequencies are computed on the host in double and passed by
+// value; here each angle is formed in double.
 //
 // Two storage forms:
 //   packed fp16 (the attention kernels): one dword per pair, cos in the low
@@ -20,13 +20,13 @@
 namespace flux {
 
 template <bool PACKED16>
-__global__ void rope_table_kernel(const int32_t* __restrict__ pos, const double* __restrict__ freq,
+__global__ void rope_table_kernel(const int32_t* __restrict__ pos, const RopeFreq freq,
                                   void* __restrict__ table, int n_tokens, int half, int p0, int p1) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n_tokens * half) return;
   const int n = idx / half, p = idx - n * half;
   const int axis = p < p0 ? 0 : (p < p0 + p1 ? 1 : 2);
-  const double ang = (double)pos[3 * n + axis] * freq[p];
+  const double ang = (double)pos[3 * n + axis] * freq.f[p];
   if constexpr (PACKED16) {
     // The angle is reduced to [-pi, pi] in double and evaluated in fp32:
     // error ~1e-7, far below the fp16 rounding (2^-12) that follows.
@@ -45,7 +45,7 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ pos, const double*
 }
 
 template <bool PACKED16>
-static hipError_t launch_table(const int32_t* pos, const double* freq, void* table, int n_tokens, int head_dim,
+static hipError_t launch_table(const int32_t* pos, const RopeFreq& freq, void* table, int n_tokens, int head_dim,
                                int d0, int d1, hipStream_t stream) {
   const int half = head_dim / 2;
   const int total = n_tokens * half;
@@ -55,12 +55,12 @@ static hipError_t launch_table(const int32_t* pos, const double* freq, void* tab
   return hipGetLastError();
 }
 
-hipError_t launch_rope_table(const int32_t* pos, const double* freq, uint32_t* table, int n_tokens,
+hipError_t launch_rope_table(const int32_t* pos, const RopeFreq& freq, uint32_t* table, int n_tokens,
                              int head_dim, int d0, int d1, hipStream_t stream) {
   return launch_table<true>(pos, freq, table, n_tokens, head_dim, d0, d1, stream);
 }
 
-hipError_t launch_rope_table_f32(const int32_t* pos, const double* freq, float2* table, int n_tokens,
+hipError_t launch_rope_table_f32(const int32_t* pos, const RopeFreq& freq, float2* table, int n_tokens,
                                  int head_dim, int d0, int d1, hipStream_t stream) {
   return launch_table<false>(pos, freq, table, n_tokens, head_dim, d0, d1, stream);
 }
