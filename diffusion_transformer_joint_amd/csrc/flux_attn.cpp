@@ -114,6 +114,50 @@ bool plan_live(const flux_attn_plan* p) {
 
 }  // namespace
 
+// Scratch memory of the allocation-free forward (flux_attn_forward_noalloc):
+// the RoPE table and the split partials of one call.  Every device that loads
+// the library holds its own copy until the process ends.  In host code the
+// name `scratch` is only a stand-in: kernels get the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) char scratch[FLUX_ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` and compute-unit count, per device ordinal,
+// looked up on the first allocation-free call on that device.  A fixed table:
+// the lookup itself allocates no host or device memory.
+constexpr int kMaxDevices = 64;
+struct ScratchDevice {
+  bool ready;
+  void* ptr;
+  int num_cus;
+};
+std::mutex g_scratch_mu;
+ScratchDevice g_scratch[kMaxDevices];
+
+int noalloc_scratch(int dev, ScratchDevice* out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FLUX_ATTN_UNSUPPORTED, "device ordinal %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchDevice& sd = g_scratch[dev];
+  if (!sd.ready) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(FLUX_ATTN_DEVICE_ERROR, "scratch has no address on device %d", dev);
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    sd.ptr = ptr;
+    sd.num_cus = cus;
+    sd.ready = true;
+  }
+  *out = sd;
+  return FLUX_ATTN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int flux_attn_abi_version(void) { return FLUX_ATTN_ABI_VERSION; }
@@ -521,6 +565,44 @@ int flux_attn_forward_segment_local(flux_attn_plan* plan, const void* q, const v
                                     const int32_t* pos_ids, void* out, void* hip_stream) {
   return forward_impl(plan, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out, false, nullptr,
                       hip_stream);
+}
+
+int flux_attn_forward_noalloc(const flux_attn_config* cfg, const void* q, const void* k, const void* v,
+                              const float* qkv_scale, const int32_t* segment_tokens, int32_t num_segments,
+                              const int32_t* pos_ids, void* out, void* hip_stream) {
+  int st = flux_attn_validate_forward(cfg, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out);
+  if (st) return st;
+  const flux_attn_config& c = *cfg;
+  long long n = 0;
+  for (int i = 0; i < num_segments; ++i) n += segment_tokens[i];
+  // Scratch layout: [RoPE table | partial O | partial (m, l)], each 256-byte
+  // aligned.  The table must fit; what is left bounds the split pieces.
+  const size_t table_bytes = ((size_t)n * (c.head_dim / 2) * 4 + 255) & ~(size_t)255;
+  const size_t cap = FLUX_ATTN_NOALLOC_SCRATCH_BYTES;
+  if (table_bytes > cap)
+    return fail(FLUX_ATTN_UNSUPPORTED,
+                "%lld tokens need a %zu-byte RoPE table; the allocation-free scratch holds %zu bytes "
+                "(at most %zu tokens at head_dim %d)",
+                n, table_bytes, cap, cap / ((size_t)c.head_dim * 2), c.head_dim);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  ScratchDevice sd{};
+  st = noalloc_scratch(dev, &sd);
+  if (st) return st;
+  char* const base = static_cast<char*>(sd.ptr);
+  const size_t piece_o = (size_t)256 * c.head_dim * sizeof(float), piece_ml = (size_t)256 * sizeof(float2);
+  long pieces = (long)((cap - table_bytes) / (piece_o + piece_ml));
+  pieces = std::min(pieces, 4L * sd.num_cus);
+  FwdWorkspace ws{};
+  ws.rope = reinterpret_cast<uint32_t*>(base);
+  ws.part_o = reinterpret_cast<float*>(base + table_bytes);
+  ws.part_ml = reinterpret_cast<float2*>(base + table_bytes + (size_t)pieces * piece_o);
+  ws.max_pieces = (int)pieces;
+  ws.num_cus = sd.num_cus;
+  ws.sched_mode = 1;  // whole tiles + split pieces only: the persistent split needs 2 slots per CU
+  return launch_forward(c, rope_freq(c), ws, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out,
+                        true, nullptr, static_cast<hipStream_t>(hip_stream), nullptr);
 }
 
 int flux_attn_forward_lse(flux_attn_plan* plan, const void* q, const void* k, const void* v,

@@ -72,6 +72,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flux_attn_create": ([cp, ctypes.POINTER(_vp)], ctypes.c_int),
         "flux_attn_forward": ([_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp], ctypes.c_int),
         "flux_attn_forward_segment_local": ([_vp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp], ctypes.c_int),
+        "flux_attn_forward_noalloc": ([cp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp], ctypes.c_int),
         "flux_attn_get_config": ([_vp, cp], ctypes.c_int),
         "flux_attn_destroy": ([_vp], ctypes.c_int),
         "flux_attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -157,6 +158,41 @@ def _device_tensor(name, t, device, shape=None, dtype=None):
         raise FluxAttnError(INVALID_ARGUMENT, f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise FluxAttnError(INVALID_ARGUMENT, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # FLUX_ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(config: Config, q, k, v, segment_tokens: Sequence[int], pos_ids, out, scales=None,
+                    stream=None):
+    """Joint attention through ``flux_attn_forward_noalloc``: no plan and no
+    device allocation (the library's static scratch holds the RoPE table and
+    split partials).  ``config`` comes from ``default_config``; the tensors are
+    as for ``Plan.forward`` and ``out`` must be given.  Returns out."""
+    import torch
+
+    fp8 = config.dtype == FP8_E4M3
+    want = (torch.uint8, torch.float8_e4m3fn) if fp8 else torch.bfloat16
+    n = int(sum(segment_tokens))
+    shape = (config.batch, n, config.num_heads, config.head_dim)
+    if not q.is_cuda:
+        raise FluxAttnError(INVALID_ARGUMENT, f"q must be a device tensor (got {q.device})")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _device_tensor(name, t, q.device, shape, want)
+    _device_tensor("pos_ids", pos_ids, q.device, (n, 3), torch.int32)
+    _device_tensor("out", out, q.device, shape, torch.bfloat16)
+    sp = None
+    if scales is not None:
+        _device_tensor("scales", scales, q.device, (3, config.batch, config.num_heads), torch.float32)
+        sp = scales.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = load_library()
+    segs = _i32_array(segment_tokens)
+    check(lib.flux_attn_forward_noalloc(ctypes.byref(config), q.data_ptr(), k.data_ptr(), v.data_ptr(), sp, segs,
+                                        len(segment_tokens), pos_ids.data_ptr(), out.data_ptr(),
+                                        stream.cuda_stream), "forward_noalloc")
+    return out
 
 
 class Plan:

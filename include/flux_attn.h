@@ -39,6 +39,7 @@
 #ifndef FLUX_ATTN_H
 #define FLUX_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -133,6 +134,27 @@ int flux_attn_forward_segment_local(flux_attn_plan* plan, const void* q, const v
                                     const float* qkv_scale, const int32_t* segment_tokens,
                                     int32_t num_segments, const int32_t* pos_ids, void* out,
                                     void* hip_stream);
+
+/* Allocation-free joint forward, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same computation and arguments as flux_attn_forward,
+ * without a plan: cfg (host) is validated as flux_attn_create does, and its
+ * max_tokens only bounds N.  The RoPE table and the split partials live in a
+ * static device array of FLUX_ATTN_NOALLOC_SCRATCH_BYTES (32 MiB) that every
+ * device holds from the library's load until the process ends; the first call
+ * on a device looks up its address there.  No call allocates host or device
+ * memory.  Limit: the table, N x head_dim x 2 bytes, must fit in the array
+ * (N <= 131,072 at head_dim 128, 262,144 at 64), FLUX_ATTN_UNSUPPORTED
+ * otherwise; the rest of the array bounds how finely the last round of query
+ * tiles is split, so results agree with flux_attn_forward to rounding, not
+ * always bitwise.  Nothing is read from an earlier call.  All calls on one
+ * device share its array: calls on one stream are ordered and safe, calls
+ * that overlap on one device (several streams or threads) race and give wrong
+ * results.  Not timed (no events). */
+#define FLUX_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int flux_attn_forward_noalloc(const flux_attn_config* cfg, const void* q, const void* k, const void* v,
+                              const float* qkv_scale, const int32_t* segment_tokens, int32_t num_segments,
+                              const int32_t* pos_ids, void* out, void* hip_stream);
 
 /* Training: forward with the per-row log-sum-exp, and the backward.  The
  * attention backward is the adjacent training workload (LoRA fine-tuning of
