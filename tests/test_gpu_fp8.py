@@ -18,12 +18,37 @@ pytestmark = pytest.mark.gpu
 S = I.Segment
 
 
+def _gen4k_rows(n, seed=7, total=640):
+    """Rows of the 66,048-token call: every wave-boundary position class of a
+    256-row query tile (rows 0, 1, 31-33, 63-65, ..., 255) in the first tiles,
+    the text/image boundary, the middle, the tiles whose K/V range the
+    schedule splits into pieces (the last 48 query tiles of the last head:
+    tiles 210-257 of its 258) and the last tile; then seeded random rows."""
+    cls = sorted({0, 1, 254, 255} | {32 * w + d for w in range(1, 8) for d in (-1, 0, 1)})
+    tiles = [0, 1, 2, 129, 130, 209, 210, 211, 233, 234, 256, 257]
+    rows = {t * 256 + r for t in tiles for r in cls}
+    rows |= {510, 511, 512, 513, n - 1}
+    rng = np.random.default_rng(seed)
+    while len(rows) < total:
+        rows.add(int(rng.integers(0, n)))
+    return np.array(sorted(r for r in rows if r < n))
+
+
 def test_gen4k_fp8_sampled_rows():
+    import time
     inp = I.make_inputs(I.WORKLOADS["gen4k_fp8"])
     got = out_fp64(run_hip(inp))
     assert np.all(np.isfinite(got))
-    rows = sample_rows(inp.workload.tokens, seed=7, count=48)
-    assert_close(got[:, rows], ref_rows(inp, rows), FP8_TOL, f"gen4k_fp8 ({len(rows)} rows)")
+    rows = _gen4k_rows(inp.workload.tokens)
+    assert len(rows) >= 512
+    t0 = time.perf_counter()
+    ref = ref_rows(inp, rows)
+    say(f"  oracle over {len(rows)} rows x 24 heads took {time.perf_counter() - t0:.1f} s")
+    assert_close(got[:, rows], ref, FP8_TOL, f"gen4k_fp8 ({len(rows)} rows)")
+    # the split pieces: last head, query tiles 210..257
+    sel = rows >= 210 * 256
+    assert sel.sum() >= 100
+    assert_close(got[:, rows[sel], 23:], ref[:, sel, 23:], FP8_TOL, "gen4k_fp8 split tiles (head 23)")
 
 
 FP8_CASES = [

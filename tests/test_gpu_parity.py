@@ -2,10 +2,11 @@
 
 Element-wise comparison on the same seeded inputs; tolerances are those the
 workload specification states for bf16 (max-abs 2e-2, relative L2 5e-3) and
-FP8 (6e-2, 2e-2).  Full outputs at sizes the oracle finishes in seconds
-(several 256-row query tiles and 64-key tiles, ragged tails); sampled rows at
-the full 8,704- and 25,088-token sizes, computed in the same launch
-configuration the benchmark times.
+FP8 (6e-2, 2e-2).  Every bf16 workload is compared over its whole output
+tensor, in the launch configuration the benchmark times: 80, 4,608, 8,704
+(about 10 s of oracle) and 25,088 tokens (about a minute of oracle on 16
+cores); ragged and special shapes at sizes that span several 256-row query
+tiles and 64-key tiles.
 """
 import numpy as np
 import pytest
@@ -20,20 +21,23 @@ pytestmark = pytest.mark.gpu
 S = I.Segment
 
 
-@pytest.mark.parametrize("name", ["tiny", "t2i1024"])
+@pytest.mark.parametrize("name", ["tiny", "t2i1024", "edit1024", "gen2048r2"])
 def test_workload_full(name):
-    inp = I.make_inputs(I.WORKLOADS[name])
-    got = out_fp64(run_hip(inp))
-    assert_close(got, ref_full(inp), BF16_TOL, name)
-
-
-@pytest.mark.parametrize("name", ["edit1024", "gen2048r2"])
-def test_workload_sampled_rows(name):
+    # whole output tensor against the whole fp64 oracle
+    import time
     inp = I.make_inputs(I.WORKLOADS[name])
     got = out_fp64(run_hip(inp))
     assert np.all(np.isfinite(got))
-    rows = sample_rows(inp.workload.tokens, seed=3)
-    assert_close(got[:, rows], ref_rows(inp, rows), BF16_TOL, f"{name} ({len(rows)} rows)")
+    say(f"  oracle over the whole {name} call ({inp.workload.tokens} tokens)...")
+    t0 = time.perf_counter()
+    ref = ref_full(inp)
+    say(f"  oracle took {time.perf_counter() - t0:.1f} s")
+    assert_close(got, ref, BF16_TOL, f"{name} (all {got.shape[1]} rows)")
+    # the worst head must also be within the bound, not only the average
+    d = got - ref
+    worst = max(float(np.linalg.norm(d[:, :, h]) / np.linalg.norm(ref[:, :, h])) for h in range(ref.shape[2]))
+    say(f"  {name}: worst head rel-L2 {worst:.3e}")
+    assert worst <= BF16_TOL[1]
 
 
 RAGGED = [
@@ -55,15 +59,25 @@ def test_ragged_shapes(name, heads, d, segs):
     assert_close(got, ref_full(inp), BF16_TOL, name)
 
 
-def test_batch_two_and_ulysses_share():
-    # B = 2, and the per-GPU share of an 8-way head split (3 of 24 heads) at full N
+def test_batch_two():
     inp = I.make_inputs(custom("b2", 3, 128, [S("text", 100), S("image", 20, 20)], batch=2))
     assert_close(out_fp64(run_hip(inp)), ref_full(inp), BF16_TOL, "batch 2")
-    inp = I.make_inputs(custom("h3_n8704", 3, 128, [S("text", 512), S("image", 64, 64),
-                                                    S("ref", 64, 64, 1)]))
+
+
+@pytest.mark.parametrize("heads", [3, 6, 12])
+def test_head_share_full(heads):
+    # One GPU's share of the 8,704-token call when its 24 heads are split over
+    # 8, 4 or 2 GPUs: 102, 204 or 408 query tiles for 256 compute units.  The
+    # library picks the persistent split for 3 and 6 heads (fewer tiles than
+    # units) and whole tiles plus split pieces for 12; whole output tensor.
+    from diffusion_transformer_joint_amd import flux_attn as fa
+    tiles = heads * 34
+    s = fa.schedule(tiles, 136, 256, 1024)
+    say(f"  {heads} heads: {tiles} tiles, split schedule {s}")
+    inp = I.make_inputs(custom(f"h{heads}_n8704", heads, 128, [S("text", 512), S("image", 64, 64),
+                                                               S("ref", 64, 64, 1)], seed=30 + heads))
     got = out_fp64(run_hip(inp))
-    rows = sample_rows(8704, seed=5, count=64)
-    assert_close(got[:, rows], ref_rows(inp, rows), BF16_TOL, "3 heads x 8704")
+    assert_close(got, ref_full(inp), BF16_TOL, f"{heads} heads x 8704 (all rows)")
 
 
 def test_peaked_scores_exercise_rescaling():
