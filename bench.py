@@ -5,30 +5,40 @@
 
 One step is one pass of the whole hot path over one batch of synthetic input:
 the RoPE angle table plus the joint attention kernel (RoPE fused into its Q/K
-loads, online softmax, bf16 MFMA), through the C ABI.  The timed workload is the
-1024^2 single-reference edit call: 512 text + 4,096 image + 4,096 reference
-tokens (8,704), 24 heads, head_dim 128, bf16 Q/K/V ~ N(0, 0.25).  Inputs are
-resident in HBM before timing starts.  The 4,608-token text-to-image call, the
-66,048-token e4m3 call, the edit call in segment-local mode (each segment
-attending to itself), one GPU's share of the edit call under 8-way head
-sharding (3 heads, persistent split schedule), the edit call with cold
-caches (a 512 MiB buffer written before each call, so Q, K, V come from HBM
-rather than the 256 MB MALL), tile-sparse attention on edit-call tokens with
-position-local attention (thresholds 0.1 and 0.01), the attention backward
-(dq, dk, dv) of the edit call and, with --all, the 25,088-token call are
-reported as extra fields of the same JSON line.  Kernel times are the mean of
-the library's per-call HIP event pairs; the median and minimum are reported
-beside it.
+loads, online softmax, bf16 MFMA) and the exact merge of its split pieces,
+through the C ABI.  The timed workload is the 1024^2 single-reference edit
+call: 512 text + 4,096 image + 4,096 reference tokens (8,704), 24 heads,
+head_dim 128, bf16 Q/K/V ~ N(0, 0.25).  Inputs are resident in HBM before
+timing starts.  W untimed calls precede exactly K timed ones, bracketed by
+device synchronisations.
+
+Extra fields of the same JSON line (each with its own timing):
+  * the other four workloads: 4,608-token text-to-image call (same K and W as
+    the headline), the 80-token tiny call, the 25,088-token 2048^2 call with
+    two references, the 66,048-token e4m3 call;
+  * one GPU's share of the edit call when its heads are split over 8, 4 or 2
+    GPUs (3, 6 and 12 heads);
+  * the edit call in segment-local mode, with cold caches, its backward, and
+    tile-sparse attention on edit-call tokens with position-local attention.
+Per workload: seed, SHA-256 of the input bytes, attention-kernel time (mean of
+the library's per-call HIP event pairs on the launch stream; median and
+minimum beside it), kernel plus merge time, and the average shader clock the
+kernel's workgroups ran at (s_memtime / s_memrealtime, measured inside the
+kernel).  The cpu_baseline leg times the fp64 oracle on the whole edit call
+and, from the same oracle, reports max-abs and relative L2 error of each
+workload's GPU output (whole tensor at 80, 4,608 and 8,704 tokens, sampled
+rows beyond).
 
 Rank 0 prints one JSON line.  Only one GPU is supported: the path shards over
 heads with no communication inside the kernel; one GPU's share is among the
 extra fields.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
-import statistics
 import os
+import statistics
 import sys
 import time
 
@@ -38,11 +48,12 @@ sys.path.insert(0, ROOT)
 METRIC = "joint-attention TFLOP/s and % MFMA peak at 4,608 and 8,704 tokens, 1 GPU"
 BF16_PEAK = 2516.6   # TFLOP/s, MI355X dense bf16 MFMA (published)
 FP8_PEAK = 5033.2    # TFLOP/s, MI355X dense fp8 MFMA (published)
-HBM_PEAK = 8000.0    # GB/s
+MIXED_CEIL = 2.0 / (1.0 / FP8_PEAK + 1.0 / BF16_PEAK)  # QK^T at the fp8 rate, PV at the bf16 rate
 PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc")
 KERNEL_SOURCES = {
-    "attn_bf16": os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc", "attn_bf16.hip"),
-    "attn_fp8": os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc", "attn_fp8.hip"),
+    "attn_bf16": os.path.join(CSRC, "attn_bf16.hip"),
+    "attn_fp8": os.path.join(CSRC, "attn_fp8.hip"),
 }
 
 
@@ -55,8 +66,7 @@ def source_sha(kernel):
     if not os.path.exists(p):
         return None
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "diffusion_transformer_joint_amd", "csrc")
-    for f in (p, os.path.join(csrc, "attn_common.h"), os.path.join(csrc, "device_common.h")):
+    for f in (p, os.path.join(CSRC, "attn_common.h"), os.path.join(CSRC, "device_common.h")):
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
@@ -68,7 +78,7 @@ def recorded_traffic(kernel, workload):
         return None
     vals = {}
     for line in open(path):
-        if ":" in line:
+        if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha256") != source_sha(kernel):
@@ -79,13 +89,8 @@ def recorded_traffic(kernel, workload):
         return None
 
 
-def measure(workload, steps, warmup, mode="joint"):
+def _device_inputs(inp):
     import torch
-    from diffusion_transformer_joint_amd import inputs as I
-    from diffusion_transformer_joint_amd.flux_attn import Plan
-
-    w = I.WORKLOADS[workload] if isinstance(workload, str) else workload
-    inp = I.make_inputs(w)
     dev = torch.device("cuda:0")
     if inp.scales is None:
         cv = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
@@ -93,9 +98,19 @@ def measure(workload, steps, warmup, mode="joint"):
     else:
         cv = lambda a: torch.from_numpy(a).to(dev)
         sc = torch.from_numpy(inp.scales).to(dev)
-    q, k, v = cv(inp.q), cv(inp.k), cv(inp.v)
-    pos = torch.from_numpy(inp.pos).to(dev)
-    out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    return cv(inp.q), cv(inp.k), cv(inp.v), torch.from_numpy(inp.pos).to(dev), sc
+
+
+def measure(w, steps, warmup, mode="joint", keep_output=False):
+    """Time `steps` forward calls of workload w after `warmup` untimed ones."""
+    import numpy as np
+    import torch
+    from diffusion_transformer_joint_amd import inputs as I
+    from diffusion_transformer_joint_amd.flux_attn import Plan
+
+    inp = I.make_inputs(w)
+    q, k, v, pos, sc = _device_inputs(inp)
+    out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda:0")
     plan = Plan(w.batch, w.heads, w.head_dim, w.tokens, dtype="fp8" if w.fp8 else "bf16")
     segs = w.segment_tokens
     for _ in range(warmup):
@@ -112,24 +127,34 @@ def measure(workload, steps, warmup, mode="joint"):
     e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kernel_ms = plan.timing_read()
+    tm = plan.timing_read(with_merge=True)
     plan.close()
     step_ms = e0.elapsed_time(e1) / steps
     if mode == "joint":
         flops = w.flops()
     else:  # each segment attends to itself
         flops = 4.0 * w.batch * w.heads * w.head_dim * sum(n * n for n in segs)
-    kavg = sum(kernel_ms) / len(kernel_ms)
-    return {
-        "workload": w.name if mode == "joint" else f"{w.name} ({mode})", "mode": mode, "tokens": w.tokens, "heads": w.heads, "head_dim": w.head_dim, "batch": w.batch,
-        "dtype": "fp8_e4m3" if w.fp8 else "bf16", "flops": flops,
+    ka, kt = tm["attn_ms"], tm["total_ms"]
+    kavg, tavg = sum(ka) / len(ka), sum(kt) / len(kt)
+    r = {
+        "workload": w.name if mode == "joint" else f"{w.name} ({mode})", "mode": mode, "tokens": w.tokens,
+        "heads": w.heads, "head_dim": w.head_dim, "batch": w.batch, "dtype": "fp8_e4m3" if w.fp8 else "bf16",
+        "seed": w.seed, "input_sha256": inp.sha256(), "steps": steps, "warmup": warmup, "flops": flops,
         "ms_per_step": step_ms, "wall_ms_per_step": (t1 - t0) * 1e3 / steps,
-        "kernel_ms_avg": kavg, "kernel_ms_min": min(kernel_ms), "kernel_ms_median": statistics.median(kernel_ms),
+        "kernel_ms_avg": kavg, "kernel_ms_min": min(ka), "kernel_ms_median": statistics.median(ka),
+        "kernel_plus_merge_ms_avg": tavg, "clock_mhz": tm["clock_mhz"],
         "tflops": flops / (step_ms * 1e-3) / 1e12, "kernel_tflops": flops / (kavg * 1e-3) / 1e12,
+        "kernel_plus_merge_tflops": flops / (tavg * 1e-3) / 1e12,
     }
+    r["frac_bf16_peak"] = r["kernel_tflops"] / BF16_PEAK
+    if w.fp8:
+        r["frac_fp8_peak"] = r["kernel_tflops"] / FP8_PEAK
+        r["frac_mixed_ceiling"] = r["kernel_tflops"] / MIXED_CEIL
+    output = out.view(torch.int16).cpu().numpy().view(np.uint16) if keep_output else None
+    return r, inp, output
 
 
-def measure_cold(workload, calls, flush_mib=512):
+def measure_cold(w, calls, flush_mib=512):
     """The joint call with cold caches: before each call a buffer of flush_mib
     MiB (twice the 256 MB MALL) is overwritten, so Q, K, V and the RoPE table
     come from HBM.  The library's event pair brackets the attention kernel
@@ -138,14 +163,10 @@ def measure_cold(workload, calls, flush_mib=512):
     from diffusion_transformer_joint_amd import inputs as I
     from diffusion_transformer_joint_amd.flux_attn import Plan
 
-    w = I.WORKLOADS[workload]
     inp = I.make_inputs(w)
-    dev = torch.device("cuda:0")
-    cv = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
-    q, k, v = cv(inp.q), cv(inp.k), cv(inp.v)
-    pos = torch.from_numpy(inp.pos).to(dev)
-    out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-    flush = torch.empty(flush_mib << 18, dtype=torch.float32, device=dev)
+    q, k, v, pos, _ = _device_inputs(inp)
+    out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda:0")
+    flush = torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda:0")
     plan = Plan(w.batch, w.heads, w.head_dim, w.tokens)
     plan.forward(q, k, v, w.segment_tokens, pos, out=out)
     torch.cuda.synchronize()
@@ -154,16 +175,17 @@ def measure_cold(workload, calls, flush_mib=512):
         flush.fill_(float(i))
         plan.forward(q, k, v, w.segment_tokens, pos, out=out)
     torch.cuda.synchronize()
-    kernel_ms = plan.timing_read()
+    tm = plan.timing_read(with_merge=True)
     plan.close()
-    med = statistics.median(kernel_ms)
+    med = statistics.median(tm["attn_ms"])
     return {"workload": f"{w.name} (cold caches: {flush_mib} MiB written before each call)", "tokens": w.tokens,
             "heads": w.heads, "head_dim": w.head_dim, "batch": w.batch, "dtype": "bf16", "flops": w.flops(),
-            "calls": calls, "kernel_ms_median": med, "kernel_ms_min": min(kernel_ms),
-            "kernel_tflops_median": w.flops() / (med * 1e-3) / 1e12, "frac_bf16_peak": w.flops() / (med * 1e-3) / 1e12 / BF16_PEAK}
+            "calls": calls, "kernel_ms_median": med, "kernel_ms_min": min(tm["attn_ms"]),
+            "clock_mhz": tm["clock_mhz"], "kernel_tflops_median": w.flops() / (med * 1e-3) / 1e12,
+            "frac_bf16_peak": w.flops() / (med * 1e-3) / 1e12 / BF16_PEAK}
 
 
-def measure_sparse(workload, tau, steps, warmup):
+def measure_sparse(w, tau, steps, warmup):
     """Tile-sparse attention: the tile mask of threshold tau (built and timed
     once), then forward_sparse timed like forward."""
     import numpy as np
@@ -171,13 +193,9 @@ def measure_sparse(workload, tau, steps, warmup):
     from diffusion_transformer_joint_amd import inputs as I
     from diffusion_transformer_joint_amd.flux_attn import Plan
 
-    w = I.WORKLOADS[workload]
     inp = I.make_inputs(w)
-    dev = torch.device("cuda:0")
-    cv = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
-    q, k, v = cv(inp.q), cv(inp.k), cv(inp.v)
-    pos = torch.from_numpy(inp.pos).to(dev)
-    out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    q, k, v, pos, _ = _device_inputs(inp)
+    out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda:0")
     plan = Plan(w.batch, w.heads, w.head_dim, w.tokens)
     segs = w.segment_tokens
     mask = plan.block_mask(q, k, segs, pos, tau)
@@ -207,7 +225,6 @@ def measure_sparse(workload, tau, steps, warmup):
     keys_per_kt = np.minimum(64, n - 64 * np.arange(m.shape[3]))
     kept_pairs = float(np.einsum("bhqk,q,k->", m.astype(np.float64), rows_per_qt, keys_per_kt))
     kavg = sum(kernel_ms) / len(kernel_ms)
-    dense_flops = w.flops()
     kept_flops = 4.0 * w.head_dim * kept_pairs
     return {
         "workload": f"{w.name} (tile-sparse, tau {tau})", "tokens": n, "heads": w.heads, "head_dim": w.head_dim,
@@ -215,11 +232,11 @@ def measure_sparse(workload, tau, steps, warmup):
         "kept_pair_fraction": kept_pairs / (w.batch * w.heads * n * n),
         "mask_ms": mask_ms, "ms_per_step": step_ms, "kernel_ms_avg": kavg,
         "flops": kept_flops, "kernel_tflops": kept_flops / (kavg * 1e-3) / 1e12,
-        "dense_equivalent_tflops": dense_flops / (kavg * 1e-3) / 1e12,
+        "dense_equivalent_tflops": w.flops() / (kavg * 1e-3) / 1e12,
     }
 
 
-def measure_backward(workload, steps, warmup):
+def measure_backward(w, steps, warmup):
     """Training forward (with the row log-sum-exp) and the backward, timed apart.
     Backward flops follow the usual count of five N x N x D products
     (recomputed S, dP, dV, dQ, dK): 2.5 x the forward's."""
@@ -228,14 +245,11 @@ def measure_backward(workload, steps, warmup):
     from diffusion_transformer_joint_amd import inputs as I
     from diffusion_transformer_joint_amd.flux_attn import Plan
 
-    w = I.WORKLOADS[workload]
     inp = I.make_inputs(w)
-    dev = torch.device("cuda:0")
-    cv = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
-    q, k, v = cv(inp.q), cv(inp.k), cv(inp.v)
-    pos = torch.from_numpy(inp.pos).to(dev)
+    q, k, v, pos, _ = _device_inputs(inp)
     rng = np.random.default_rng(99)
-    do = cv(I.f32_to_bf16_bits(rng.standard_normal(inp.q.shape, dtype=np.float32) * np.float32(0.5)))
+    do = torch.from_numpy(I.f32_to_bf16_bits(rng.standard_normal(inp.q.shape, dtype=np.float32) *
+                                             np.float32(0.5)).view("int16")).view(torch.bfloat16).to("cuda:0")
     plan = Plan(w.batch, w.heads, w.head_dim, w.tokens)
     segs = w.segment_tokens
     out, lse = plan.forward_lse(q, k, v, segs, pos)
@@ -259,35 +273,65 @@ def measure_backward(workload, steps, warmup):
             "kernel_tflops": flops / (kavg * 1e-3) / 1e12, "frac_bf16_peak": flops / (kavg * 1e-3) / 1e12 / BF16_PEAK}
 
 
-def cpu_baseline(workload, rows_count):
-    """The fp64 oracle, as it stands, on a bounded sample of query rows."""
+def _bf16_out_fp64(bits):
+    import numpy as np
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def cpu_baseline(main_inp, main_out, checks):
+    """The cpu_baseline leg: the fp64 oracle, as it stands, timed on the whole
+    headline call (its output also gives the headline's error), then the same
+    oracle on the other workloads' outputs (whole tensors up to 4,608 tokens,
+    sampled rows beyond) for their error fields."""
     import numpy as np
     import oracle
-    from diffusion_transformer_joint_amd import inputs as I
 
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    w = I.WORKLOADS[workload]
-    inp = I.make_inputs(w)
-    q, k, v = oracle.inputs_to_fp64(inp)
-    rows = np.linspace(0, w.tokens - 1, rows_count).astype(np.int64)
+
+    def errors(got, ref):
+        d = got - ref
+        return {"max_abs": float(np.abs(d).max()), "rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref))}
+
+    w = main_inp.workload
+    q, k, v = oracle.inputs_to_fp64(main_inp)
     t0 = time.perf_counter()
-    oracle.joint_rope_attention_rows(q, k, v, inp.pos, w.axes_dim, rows)
+    ref = oracle.joint_rope_attention(q, k, v, main_inp.pos, w.axes_dim)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.batch * w.heads * len(rows) * w.tokens * w.head_dim
+    main_err = dict(errors(_bf16_out_fp64(main_out), ref), rows="all")
+    del q, k, v, ref
+    flops = w.flops()
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "seconds": round(dt, 2), "gflops": round(flops / dt / 1e9, 1), "cpu": cpu,
-            "sample": f"{len(rows)} of {w.tokens} query rows, all {w.heads} heads, full K/V "
-                      f"(RoPE of all keys included), {workload}; {dt:.1f} s"}
+            "sample": f"the whole {w.name} call: all {w.tokens} query rows, all {w.heads} heads, full K/V "
+                      f"(RoPE of all keys included); {dt:.1f} s"}
+    log(f"cpu_baseline: oracle {dt:.1f} s on {cores} threads; {w.name} max-abs {main_err['max_abs']:.3e} "
+        f"rel-L2 {main_err['rel_l2']:.3e}")
+    out_err = {}
+    for name, (inp, got_bits) in checks.items():
+        wl = inp.workload
+        qq, kk, vv = oracle.inputs_to_fp64(inp)
+        got = _bf16_out_fp64(got_bits)
+        if wl.tokens <= 4608:
+            e = dict(errors(got, oracle.joint_rope_attention(qq, kk, vv, inp.pos, wl.axes_dim)), rows="all")
+        else:
+            n = wl.tokens
+            rows = np.unique(np.concatenate([np.linspace(0, n - 1, 192).astype(np.int64),
+                                             np.random.default_rng(wl.seed).integers(0, n, 64)]))
+            refr = oracle.joint_rope_attention_rows(qq, kk, vv, inp.pos, wl.axes_dim, rows)
+            e = dict(errors(got[:, rows], refr), rows=f"{len(rows)} sampled of {n}")
+        out_err[name] = e
+        log(f"  oracle check {name}: max-abs {e['max_abs']:.3e} rel-L2 {e['rel_l2']:.3e} ({e['rows']})")
+    return base, main_err, out_err
 
 
 def calibrate_copy(mb):
@@ -302,24 +346,27 @@ def calibrate_copy(mb):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
+def rnd(r):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     # 2,000 warm-up calls (~1.7 s) bring the GPU to its steady clock under this
-    # load; 50 calls after 10 read 2-3% slower, still on the way up from idle.
+    # load; short runs read slower, still on the way up from idle.
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=2000)
-    ap.add_argument("--workload", default="edit1024")
-    ap.add_argument("--all", action="store_true", help="also time the 25,088-token and FP8 workloads")
+    ap.add_argument("--only-headline", action="store_true", help="time the edit call only (profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=8704)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="only run a plain copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: joint attention shards over heads with no communication "
-              "inside the kernel, so one GPU's share (3 of 24 heads) is timed among the extra fields; run with --gpus 1.", file=sys.stderr)
+              "inside the kernel, so one GPU's share (3, 6 or 12 of 24 heads) is timed among the extra "
+              "fields; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy_mb:
         calibrate_copy(args.calibrate_copy_mb)
@@ -329,71 +376,84 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-
-    main_run = measure(args.workload, args.steps, args.warmup)
-    log(f"{args.workload}: {main_run['kernel_tflops']:.1f} TFLOP/s kernel, {main_run['ms_per_step']:.3f} ms/step")
-    extra = []
-    import dataclasses
     from diffusion_transformer_joint_amd import inputs as I
-    share = dataclasses.replace(I.WORKLOADS["edit1024"], heads=3, name="edit1024_3heads",
-                                description="one GPU's share (3 of 24 heads) of the 8,704-token edit call")
-    others = [("t2i1024", "joint"), ("gen4k_fp8", "joint"), ("edit1024", "segment_local"), (share, "joint")] + \
-        ([("gen2048r2", "joint")] if args.all else [])
-    xs, xw = min(args.steps, 50), min(args.warmup, 10)  # extra fields: short runs
-    for name, mode in others:
-        if name == args.workload and mode == "joint":
-            continue
-        r = measure(name, max(5, xs // 5) if name == "gen4k_fp8" else max(5, xs // 2),
-                    max(2, xw // 2), mode=mode)
-        r["frac_bf16_peak"] = r["kernel_tflops"] / BF16_PEAK
-        if r["dtype"] != "bf16":
-            # QK^T runs at the fp8 rate, PV at the bf16 rate (P is kept in bf16)
-            r["frac_fp8_peak"] = r["kernel_tflops"] / FP8_PEAK
-            r["frac_mixed_ceiling"] = r["kernel_tflops"] / (2.0 / (1.0 / FP8_PEAK + 1.0 / BF16_PEAK))
-        extra.append(r)
-        log(f"{r['workload']}: {r['kernel_tflops']:.1f} TFLOP/s kernel")
-    r = measure_cold(args.workload, max(5, xs // 5))
-    extra.append(r)
-    log(f"{r['workload']}: {r['kernel_tflops_median']:.1f} TFLOP/s kernel (median)")
-    r = measure_backward("edit1024", max(5, xs // 5), max(2, xw // 2))
-    extra.append(r)
-    log(f"{r['workload']}: {r['kernel_ms_avg']:.3f} ms, {r['kernel_tflops']:.1f} TFLOP/s (2.5 x forward flops)")
-    for tau in (0.1, 0.01):
-        r = measure_sparse("edit1024_local", tau, max(5, xs // 2), max(2, xw // 2))
-        r["speedup_vs_dense_edit1024"] = main_run["kernel_ms_avg"] / r["kernel_ms_avg"]
-        extra.append(r)
-        log(f"{r['workload']}: kept {r['kept_pair_fraction']:.2f} of pairs, {r['kernel_ms_avg']:.3f} ms, "
-            f"{r['kernel_tflops']:.1f} TFLOP/s on kept pairs, x{r['speedup_vs_dense_edit1024']:.2f} vs dense")
 
-    kernel = "attn_bf16"
-    traffic = recorded_traffic(kernel, args.workload)
+    K, W = args.steps, args.warmup
+    WL = I.WORKLOADS
+    main_run, main_inp, main_out = measure(WL["edit1024"], K, W, keep_output=True)
+    log(f"edit1024: {main_run['kernel_tflops']:.1f} TFLOP/s kernel, {main_run['ms_per_step']:.3f} ms/step, "
+        f"clock {main_run['clock_mhz']:.0f} MHz")
+    extra, checks = [], {}
+    if not args.only_headline:
+        share = lambda h: dataclasses.replace(WL["edit1024"], heads=h, name=f"edit1024_{h}heads",
+                                              description=f"one GPU's share ({h} of 24 heads) of the edit call")
+        runs = [
+            (WL["t2i1024"], K, W, "joint"),                       # named in the metric: same counts
+            (WL["tiny"], K, W, "joint"),
+            (WL["gen2048r2"], min(K, 100), min(W, 200), "joint"),
+            (WL["gen4k_fp8"], min(K, 20), min(W, 5), "joint"),
+            (share(3), min(K, 200), min(W, 400), "joint"),
+            (share(6), min(K, 200), min(W, 400), "joint"),
+            (share(12), min(K, 200), min(W, 400), "joint"),
+            (WL["edit1024"], min(K, 100), min(W, 200), "segment_local"),
+        ]
+        for w, k_, w_, mode in runs:
+            r, inp, out = measure(w, k_, w_, mode=mode, keep_output=(mode == "joint"))
+            if mode == "joint":
+                checks[r["workload"]] = (inp, out)
+            extra.append(r)
+            log(f"{r['workload']}: {r['kernel_tflops']:.1f} TFLOP/s kernel ({r['frac_bf16_peak']:.3f} of bf16 peak), "
+                f"clock {r['clock_mhz']:.0f} MHz")
+        r = measure_cold(WL["edit1024"], max(5, min(K, 20)))
+        extra.append(r)
+        log(f"{r['workload']}: {r['kernel_tflops_median']:.1f} TFLOP/s kernel (median)")
+        r = measure_backward(WL["edit1024"], max(5, min(K, 20)), max(2, min(W, 5)))
+        extra.append(r)
+        log(f"{r['workload']}: {r['kernel_ms_avg']:.3f} ms, {r['kernel_tflops']:.1f} TFLOP/s (2.5 x forward flops)")
+        for tau in (0.1, 0.01):
+            r = measure_sparse(WL["edit1024_local"], tau, max(5, min(K, 25)), max(2, min(W, 5)))
+            r["speedup_vs_dense_edit1024"] = main_run["kernel_ms_avg"] / r["kernel_ms_avg"]
+            extra.append(r)
+            log(f"{r['workload']}: kept {r['kept_pair_fraction']:.2f} of pairs, {r['kernel_ms_avg']:.3f} ms, "
+                f"x{r['speedup_vs_dense_edit1024']:.2f} vs dense")
+
+    traffic = recorded_traffic("attn_bf16", "edit1024")
     achieved = main_run["kernel_tflops"]
     line = {
         "metric": METRIC,
         "value": round(main_run["tflops"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": K,
+        "warmup": W,
         "ms_per_step": round(main_run["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: 1024^2 single-reference edit call, 512 text + 4096 image + "
-                               f"4096 reference tokens", "batch": main_run["batch"], "seq_len": main_run["tokens"],
-                   "heads": main_run["heads"], "head_dim": main_run["head_dim"], "parallelism": "none (1 GPU)"},
+        "config": {"workload": "edit1024: 1024^2 single-reference edit call, 512 text + 4096 image + "
+                               "4096 reference tokens", "batch": main_run["batch"], "seq_len": main_run["tokens"],
+                   "heads": main_run["heads"], "head_dim": main_run["head_dim"], "parallelism": "none (1 GPU)",
+                   "seed": main_run["seed"], "input_sha256": main_run["input_sha256"]},
         "frac_bf16_peak": round(main_run["tflops"] / BF16_PEAK, 4),
+        "clock_mhz": round(main_run["clock_mhz"], 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK, 4), "traffic": traffic,
                      "kernel": "attn_fwd_bf16_kernel<128, false>", "kernel_ms_avg": round(main_run["kernel_ms_avg"], 4),
                      "kernel_ms_median": round(main_run["kernel_ms_median"], 4),
-                     "flops_per_launch": main_run["flops"]},
-        "extra": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in extra],
+                     "flops_per_launch": main_run["flops"],
+                     "kernel_plus_merge_ms_avg": round(main_run["kernel_plus_merge_ms_avg"], 4),
+                     "frac_with_merge": round(main_run["kernel_plus_merge_tflops"] / BF16_PEAK, 4)},
+        "extra": [rnd(r) for r in extra],
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_rows)
+        base, main_err, out_err = cpu_baseline(main_inp, main_out, checks)
+        line["cpu_baseline"] = base
+        line["error_vs_oracle"] = main_err
+        for r in line["extra"]:
+            if r["workload"] in out_err:
+                r["error_vs_oracle"] = out_err[r["workload"]]
     print(json.dumps(line), flush=True)
 
 

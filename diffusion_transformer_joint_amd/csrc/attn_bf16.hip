@@ -565,7 +565,9 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     if (a.tile_order != nullptr) tile_g = a.tile_order[tile_g];
     piece = slot % a.split;
   }
+  const ClockProbe probe(a.clk);
   fwd_tile<D, SPARSE>(a, ksm, vsm, tile_g, slot, piece, -1, -1);
+  probe.finish();
 }
 
 // Persistent split (one workgroup per CU, dense): the launch's tiles x K/V
@@ -586,6 +588,7 @@ void attn_fwd_bf16_persistent_kernel(AttnArgs a) {
   const long hi = W * (cu + 1) / gridDim.x;
   long pos = W * cu / gridDim.x;
   const int first = (int)(pos / nkv);
+  const ClockProbe probe(a.clk);
   while (pos < hi) {
     const int tile_g = (int)(pos / nkv);
     const long next = hi < (long)(tile_g + 1) * nkv ? hi : (long)(tile_g + 1) * nkv;
@@ -595,6 +598,7 @@ void attn_fwd_bf16_persistent_kernel(AttnArgs a) {
     pos = next;
     if (pos < hi) __syncthreads();  // the next piece reuses the LDS buffers
   }
+  probe.finish();
 }
 
 // Merge of a persistent-split launch: block (c - 1) * 16 + sub, for each

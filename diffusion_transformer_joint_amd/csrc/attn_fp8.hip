@@ -93,12 +93,12 @@ __device__ __forceinline__ void e4m3x16_to_bf16(u32x4 x, u32x4* lo, u32x4* hi) {
   }
 }
 
+// One work item per workgroup: a whole query tile, or one K/V piece of a
+// split tile of the last round.
 template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_fp8_kernel(Fp8Args a) {
+__device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg<D>::K8TILEB],
+                                         char (&vsm)[2][Fp8Cfg<D>::VTILEB]) {
   using C = Fp8Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char ksm[2][C::K8TILEB];
-  __shared__ __attribute__((aligned(16))) char vsm[2][C::VTILEB];
 
   const int N = a.n_tokens, H = a.heads;
   const int n_tiles = (N + C::BN - 1) / C::BN;
@@ -443,6 +443,17 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
         *(u32x2*)(orow + d) = w;
       }
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_fp8_kernel(Fp8Args a) {
+  using C = Fp8Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char ksm[2][C::K8TILEB];
+  __shared__ __attribute__((aligned(16))) char vsm[2][C::VTILEB];
+  const ClockProbe probe(a.clk);
+  fp8_tile<D>(a, ksm, vsm);
+  probe.finish();
 }
 
 hipError_t launch_attn_fp8(const Fp8Args& a, int head_dim, const Schedule& sch, hipStream_t stream) {

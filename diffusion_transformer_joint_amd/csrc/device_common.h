@@ -98,6 +98,33 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32);
 }
 
+// Optional clock measurement of a workgroup: shader-clock cycles
+// (s_memtime) and constant-rate wall-clock ticks (s_memrealtime) from the
+// workgroup's start to the end of its first wave are added to dst[0] and
+// dst[1] by one thread; their ratio over a launch is the average shader clock
+// the launch's workgroups ran at.  The start values are subtracted at once
+// (unsigned sums wrap, so the totals come out right) and nothing stays live
+// across the kernel.  dst == nullptr: off (one uniform branch each).
+struct ClockProbe {
+  unsigned long long* dst;
+  __device__ __forceinline__ explicit ClockProbe(unsigned long long* d) : dst(d) {
+    if (dst != nullptr && threadIdx.x == 0) {
+      const uint64_t c0 = __builtin_amdgcn_s_memtime();
+      const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+      atomicAdd(dst, (unsigned long long)(0ull - c0));
+      atomicAdd(dst + 1, (unsigned long long)(0ull - r0));
+    }
+  }
+  __device__ __forceinline__ void finish() const {
+    if (dst != nullptr && threadIdx.x == 0) {
+      const uint64_t c1 = __builtin_amdgcn_s_memtime();
+      const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+      atomicAdd(dst, (unsigned long long)c1);
+      atomicAdd(dst + 1, (unsigned long long)r1);
+    }
+  }
+};
+
 // Tiles are dispatched round-robin over the 8 XCDs (block i runs on XCD i % 8).
 // Remap so that each XCD receives a contiguous range of logical tiles: tiles of
 // one head then share that XCD's L2.  A bijection on [0, total).

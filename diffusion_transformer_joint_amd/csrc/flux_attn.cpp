@@ -81,6 +81,8 @@ struct flux_attn_plan {
   int sched_mode = 0;  // FLUX_ATTN_SCHEDULE at creation: 0 by cost, 1 'split', 2 'persistent'
   std::vector<hipEvent_t> ev_start, ev_mid, ev_stop;  // kernel timing: attention | merge
   int timing_used = 0;
+  unsigned long long* clk = nullptr;  // while timing: shader cycles and wall ticks of the timed kernels
+  int wall_khz = 0;                   // rate of the wall-clock counter
 };
 
 namespace {
@@ -96,6 +98,8 @@ void release_timing(flux_attn_plan* p) {
   p->ev_mid.clear();
   p->ev_stop.clear();
   p->timing_used = 0;
+  (void)hipFree(p->clk);
+  p->clk = nullptr;
 }
 
 }  // namespace
@@ -404,6 +408,7 @@ struct FwdWorkspace {
   int max_pieces;
   int num_cus;
   int sched_mode;     // 0 by cost, 1 never persistent, 2 persistent where possible
+  unsigned long long* clk;  // optional clock measurement of the attention kernels
 };
 
 // Optional HIP events bracketing the call: before the attention kernel, after
@@ -476,6 +481,7 @@ int launch_forward(const flux_attn_config& c, const flux::RopeFreq& freq, const 
     a.part_o = ws.part_o;
     a.part_ml = ws.part_ml;
     a.lse = lse;
+    a.clk = ev ? ws.clk : nullptr;
     if (fp8) {
       const size_t off = (size_t)gt[0];
       flux::Fp8Args f{};
@@ -492,6 +498,7 @@ int launch_forward(const flux_attn_config& c, const flux::RopeFreq& freq, const 
       f.c = a.c;
       f.part_o = a.part_o;
       f.part_ml = a.part_ml;
+      f.clk = a.clk;
       e = flux::launch_attn_fp8(f, c.head_dim, sch, stream);
       // the e4m3 merge reads the same fields through AttnArgs: one range at
       // offset 0 of the shifted pointers
@@ -537,7 +544,7 @@ int forward_impl(flux_attn_plan* plan, const void* q, const void* k, const void*
   if (dev != plan->device)
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan was created on device %d, current device is %d", plan->device, dev);
   const FwdWorkspace ws{rope16(plan), plan->part_o, plan->part_ml, plan->max_pieces, plan->num_cus,
-                        plan->sched_mode};
+                        plan->sched_mode, plan->clk};
   const bool timed = plan->timing_used < (int)plan->ev_start.size();
   FwdEvents ev{};
   if (timed) {
@@ -601,6 +608,7 @@ int flux_attn_forward_noalloc(const flux_attn_config* cfg, const void* q, const 
   ws.max_pieces = (int)pieces;
   ws.num_cus = sd.num_cus;
   ws.sched_mode = 1;  // whole tiles + split pieces only: the persistent split needs 2 slots per CU
+  ws.clk = nullptr;
   return launch_forward(c, rope_freq(c), ws, q, k, v, qkv_scale, segment_tokens, num_segments, pos_ids, out,
                         true, nullptr, static_cast<hipStream_t>(hip_stream), nullptr);
 }
@@ -788,6 +796,7 @@ int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k,
   a.list_stride = KT;
   a.tile_order = ordered ? plan->tile_order : nullptr;
   const bool timed = plan->timing_used < (int)plan->ev_start.size();
+  a.clk = timed ? plan->clk : nullptr;
   if (timed) {
     e = hipEventRecord(plan->ev_start[plan->timing_used], stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -826,6 +835,15 @@ int flux_attn_timing_enable(flux_attn_plan* plan, int32_t capacity) {
   if (capacity < 0 || capacity > 4096)
     return fail(FLUX_ATTN_INVALID_ARGUMENT, "timing capacity %d outside [0, 4096]", capacity);
   release_timing(plan);
+  if (capacity > 0) {
+    hipError_t e = hipDeviceGetAttribute(&plan->wall_khz, hipDeviceAttributeWallClockRate, plan->device);
+    if (e == hipSuccess) e = hipMalloc(&plan->clk, 2 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipMemset(plan->clk, 0, 2 * sizeof(unsigned long long));
+    if (e != hipSuccess) {
+      release_timing(plan);
+      return hip_fail(e, "timing clock buffer");
+    }
+  }
   for (int i = 0; i < capacity; ++i) {
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     for (int j = 0; j < 3; ++j) {
@@ -843,8 +861,8 @@ int flux_attn_timing_enable(flux_attn_plan* plan, int32_t capacity) {
   return ok();
 }
 
-int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, float* total_ms, int32_t max_count,
-                          int32_t* count) {
+int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, float* total_ms, double* clock_mhz,
+                          int32_t max_count, int32_t* count) {
   if (!plan_live(plan)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "plan is NULL or destroyed");
   if (!count || (max_count > 0 && !attn_ms)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "output pointer is NULL");
   *count = 0;
@@ -859,6 +877,14 @@ int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, float* total_ms,
       if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
     }
     *count = m;
+  }
+  if (clock_mhz) *clock_mhz = 0.0;
+  if (plan->clk) {
+    unsigned long long h[2] = {0, 0};
+    hipError_t e = hipMemcpy(h, plan->clk, sizeof h, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemset(plan->clk, 0, sizeof h);
+    if (e != hipSuccess) return hip_fail(e, "timing clock read");
+    if (clock_mhz && h[1] > 0) *clock_mhz = (double)h[0] / (double)h[1] * plan->wall_khz * 1e-3;
   }
   plan->timing_used = 0;
   return ok();

@@ -34,6 +34,9 @@ struct AttnArgs {
   // Optional: natural-log log-sum-exp of each row of scale * S, [B][H][N]
   // (single-range launches).
   float* lse;
+  // Optional clock measurement: [0] += shader cycles, [1] += wall-clock ticks
+  // of every workgroup (ClockProbe).
+  unsigned long long* clk;
   // Token ranges of the launch (bf16 kernel): range r attends over tokens
   // [rng_tok0[r], rng_tok0[r] + rng_len[r]) of the sequence (q, k, v, o and
   // rope point at token 0) and owns the launch's tiles [rng_tile0[r],
@@ -83,6 +86,7 @@ struct Fp8Args {
   int split;
   float* part_o;
   float2* part_ml;
+  unsigned long long* clk;  // optional clock measurement (as AttnArgs::clk)
 };
 
 // Per-pair rotary frequencies theta^(-2j/d_a), computed on the host in double

@@ -80,8 +80,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flux_attn_abi_version": ([], ctypes.c_int),
         "flux_attn_timing_enable": ([_vp, _i32], ctypes.c_int),
         "flux_attn_schedule": ([_i32, _i32, _i32, _i32, _i32, _i32p, _i32p, _i32p, _i32p], ctypes.c_int),
-        "flux_attn_timing_read": ([_vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), _i32,
-                                   _i32p], ctypes.c_int),
+        "flux_attn_timing_read": ([_vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                   ctypes.POINTER(ctypes.c_double), _i32, _i32p], ctypes.c_int),
         "flux_attn_block_mask": ([_vp, _vp, _vp, _i32p, _i32, _vp, ctypes.c_float, _vp, _vp], ctypes.c_int),
         "flux_attn_forward_sparse": ([_vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
         "flux_attn_forward_lse": ([_vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
@@ -347,14 +347,19 @@ class Plan:
     def timing_read(self, max_count: int = 4096, with_merge: bool = False):
         """Durations (ms) of the attention kernels recorded since timing_enable/last read.
 
-        with_merge: also return the durations of attention kernel plus the merge
-        of its split pieces, as a second list."""
+        with_merge: return a dict instead: "attn_ms" (attention kernel),
+        "total_ms" (attention kernel plus the merge of its split pieces) and
+        "clock_mhz" (average shader clock of the timed attention kernels)."""
         buf = (ctypes.c_float * max_count)()
         tot = (ctypes.c_float * max_count)()
+        mhz = ctypes.c_double(0.0)
         n = ctypes.c_int32(0)
-        check(self._lib.flux_attn_timing_read(self._handle, buf, tot, max_count, ctypes.byref(n)), "timing_read")
+        check(self._lib.flux_attn_timing_read(self._handle, buf, tot, ctypes.byref(mhz), max_count, ctypes.byref(n)),
+              "timing_read")
         attn = [buf[i] for i in range(n.value)]
-        return (attn, [tot[i] for i in range(n.value)]) if with_merge else attn
+        if not with_merge:
+            return attn
+        return {"attn_ms": attn, "total_ms": [tot[i] for i in range(n.value)], "clock_mhz": mhz.value}
 
     def close(self) -> None:
         if getattr(self, "_handle", None) is not None:

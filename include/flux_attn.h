@@ -215,20 +215,24 @@ int flux_attn_forward_sparse(flux_attn_plan* plan, const void* q, const void* k,
                              const uint8_t* mask, void* out, void* hip_stream);
 
 /* Kernel timing.  flux_attn_timing_enable(plan, capacity) with capacity > 0
- * creates capacity triples of HIP events (capacity <= 4096); every following
- * forward call records one triple (none once all are used), on the stream its
- * kernels run on: before the attention kernel, after it, and after the exact
- * merge of its split pieces (if any).  For segment-local calls the first two
- * span the attention kernels of all segments (the small merge kernels between
- * them included).  capacity = 0 releases them.
+ * creates capacity triples of HIP events (capacity <= 4096) and a 16-byte
+ * device counter; every following forward call records one triple (none once
+ * all are used), on the stream its kernels run on: before the attention
+ * kernel, after it, and after the exact merge of its split pieces (if any).
+ * For segment-local calls the first two span the attention kernels of all
+ * segments (the small merge kernels between them included).  The timed
+ * attention kernels also add each workgroup's shader-clock cycles and
+ * constant-rate wall-clock ticks to the counter.  capacity = 0 releases all.
  * flux_attn_timing_read() waits for the last recorded triple, writes the
  * durations in milliseconds of up to max_count recorded calls to host arrays:
  * attn_ms[i] (attention kernel) and, if total_ms is not NULL, total_ms[i]
- * (attention kernel plus merge), then starts over.  The caller must not read
- * while another thread runs forward calls on the plan. */
+ * (attention kernel plus merge); if clock_mhz is not NULL, the average shader
+ * clock (MHz) the timed attention kernels' workgroups ran at (0 if none ran);
+ * then starts over.  The caller must not read while another thread runs
+ * forward calls on the plan. */
 int flux_attn_timing_enable(flux_attn_plan* plan, int32_t capacity);
-int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, float* total_ms, int32_t max_count,
-                          int32_t* count);
+int flux_attn_timing_read(flux_attn_plan* plan, float* attn_ms, float* total_ms, double* clock_mhz,
+                          int32_t max_count, int32_t* count);
 
 /* Work split chosen by forward() for a launch (host only, no device call).
  * The kernel runs one 256-row query tile of one (batch, head) per workgroup,
