@@ -185,9 +185,10 @@ def measure_cold(w, calls, flush_mib=512):
             "frac_bf16_peak": w.flops() / (med * 1e-3) / 1e12 / BF16_PEAK}
 
 
-def measure_sparse(w, tau, steps, warmup):
-    """Tile-sparse attention: the tile mask of threshold tau (built and timed
-    once), then forward_sparse timed like forward."""
+def measure_sparse(w, tau, steps, warmup, rule="bound"):
+    """Tile-sparse attention: the tile mask of threshold tau by `rule` (timed
+    over `steps` builds), then forward_sparse timed like forward; the
+    deviation of its output from the dense forward on the same inputs."""
     import numpy as np
     import torch
     from diffusion_transformer_joint_amd import inputs as I
@@ -198,12 +199,12 @@ def measure_sparse(w, tau, steps, warmup):
     out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda:0")
     plan = Plan(w.batch, w.heads, w.head_dim, w.tokens)
     segs = w.segment_tokens
-    mask = plan.block_mask(q, k, segs, pos, tau)
+    mask = plan.block_mask(q, k, segs, pos, tau, rule=rule)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        plan.block_mask(q, k, segs, pos, tau, mask=mask)
+        plan.block_mask(q, k, segs, pos, tau, mask=mask, rule=rule)
     e1.record()
     torch.cuda.synchronize()
     mask_ms = e0.elapsed_time(e1) / steps
@@ -217,7 +218,12 @@ def measure_sparse(w, tau, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     kernel_ms = plan.timing_read()
+    dense = plan.forward(q, k, v, segs, pos)
+    torch.cuda.synchronize()
     plan.close()
+    diff = (out.float() - dense.float())
+    dev_rel = float(torch.linalg.vector_norm(diff) / torch.linalg.vector_norm(dense.float()))
+    dev_max = float(diff.abs().max())
     step_ms = e0.elapsed_time(e1) / steps
     m = mask.cpu().numpy().astype(bool)
     n = w.tokens
@@ -227,13 +233,14 @@ def measure_sparse(w, tau, steps, warmup):
     kavg = sum(kernel_ms) / len(kernel_ms)
     kept_flops = 4.0 * w.head_dim * kept_pairs
     return {
-        "workload": f"{w.name} (tile-sparse, tau {tau})", "tokens": n, "heads": w.heads, "head_dim": w.head_dim,
-        "batch": w.batch, "dtype": "bf16", "tau": tau, "kept_tile_fraction": float(m.mean()),
-        "kept_pair_fraction": kept_pairs / (w.batch * w.heads * n * n),
+        "workload": f"{w.name} (tile-sparse, {rule} rule, tau {tau})", "tokens": n, "heads": w.heads,
+        "head_dim": w.head_dim, "batch": w.batch, "dtype": "bf16", "rule": rule, "tau": tau,
+        "kept_tile_fraction": float(m.mean()), "kept_pair_fraction": kept_pairs / (w.batch * w.heads * n * n),
         "mask_ms": mask_ms, "ms_per_step": step_ms, "kernel_ms_avg": kavg,
         "flops": kept_flops, "kernel_tflops": kept_flops / (kavg * 1e-3) / 1e12,
         "dense_equivalent_tflops": w.flops() / (kavg * 1e-3) / 1e12,
-    }
+        "deviation_from_dense_rel_l2": dev_rel, "deviation_from_dense_max_abs": dev_max,
+    }, inp, m
 
 
 def measure_backward(w, steps, warmup):
@@ -278,7 +285,7 @@ def _bf16_out_fp64(bits):
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def cpu_baseline(main_inp, main_out, checks):
+def cpu_baseline(main_inp, main_out, checks, sparse_checks):
     """The cpu_baseline leg: the fp64 oracle, as it stands, timed on the whole
     headline call (its output also gives the headline's error), then the same
     oracle on the other workloads' outputs (whole tensors up to 4,608 tokens,
@@ -331,6 +338,27 @@ def cpu_baseline(main_inp, main_out, checks):
             e = dict(errors(got[:, rows], refr), rows=f"{len(rows)} sampled of {n}")
         out_err[name] = e
         log(f"  oracle check {name}: max-abs {e['max_abs']:.3e} rel-L2 {e['rel_l2']:.3e} ({e['rows']})")
+    # score-bound sparse runs: the proven distance from dense attention,
+    # delta_i (max V - min V) per element, with delta_i the dense softmax mass
+    # of row i's skipped keys, against the oracle's sparse-vs-dense distance
+    for name, (inp, mask) in sparse_checks.items():
+        wl = inp.workload
+        qq, kk, vv = oracle.inputs_to_fp64(inp)
+        n = wl.tokens
+        rows = np.unique(np.linspace(0, n - 1, 48).astype(np.int64))
+        delta = oracle.skipped_mass(qq, kk, inp.pos, wl.axes_dim, mask)
+        bound = oracle.dense_error_bound(delta, vv)[:, rows]
+        dense = oracle.joint_rope_attention_rows(qq, kk, vv, inp.pos, wl.axes_dim, rows)
+        sparse = oracle.block_sparse_attention(qq, kk, vv, inp.pos, wl.axes_dim, mask, rows=rows)
+        dev = np.abs(sparse - dense)
+        out_err[name] = {"rows": f"{len(rows)} sampled of {n}", "max_skipped_mass": float(delta.max()),
+                         "mean_skipped_mass": float(delta.mean()),
+                         "oracle_deviation_rel_l2": float(np.linalg.norm(dev) / np.linalg.norm(dense)),
+                         "bound_rel_l2": float(np.linalg.norm(bound) / np.linalg.norm(dense)),
+                         "deviation_within_bound": bool((dev <= bound + 1e-12).all())}
+        log(f"  oracle check {name}: skipped mass max {delta.max():.3e}, deviation rel-L2 "
+            f"{out_err[name]['oracle_deviation_rel_l2']:.3e} <= bound rel-L2 {out_err[name]['bound_rel_l2']:.3e}: "
+            f"{out_err[name]['deviation_within_bound']}")
     return base, main_err, out_err
 
 
@@ -383,7 +411,7 @@ def main():
     main_run, main_inp, main_out = measure(WL["edit1024"], K, W, keep_output=True)
     log(f"edit1024: {main_run['kernel_tflops']:.1f} TFLOP/s kernel, {main_run['ms_per_step']:.3f} ms/step, "
         f"clock {main_run['clock_mhz']:.0f} MHz")
-    extra, checks = [], {}
+    extra, checks, sparse_checks = [], {}, {}
     if not args.only_headline:
         share = lambda h: dataclasses.replace(WL["edit1024"], heads=h, name=f"edit1024_{h}heads",
                                               description=f"one GPU's share ({h} of 24 heads) of the edit call")
@@ -410,12 +438,16 @@ def main():
         r = measure_backward(WL["edit1024"], max(5, min(K, 20)), max(2, min(W, 5)))
         extra.append(r)
         log(f"{r['workload']}: {r['kernel_ms_avg']:.3f} ms, {r['kernel_tflops']:.1f} TFLOP/s (2.5 x forward flops)")
-        for tau in (0.1, 0.01):
-            r = measure_sparse(WL["edit1024_local"], tau, max(5, min(K, 25)), max(2, min(W, 5)))
+        for rule, tau in (("bound", 0.1), ("bound", 0.01), ("pooled", 0.1), ("pooled", 0.01)):
+            r, sinp, smask = measure_sparse(WL["edit1024_local"], tau, max(5, min(K, 25)), max(2, min(W, 5)), rule)
             r["speedup_vs_dense_edit1024"] = main_run["kernel_ms_avg"] / r["kernel_ms_avg"]
+            r["speedup_with_mask_vs_dense_edit1024"] = main_run["kernel_ms_avg"] / (r["kernel_ms_avg"] + r["mask_ms"])
             extra.append(r)
-            log(f"{r['workload']}: kept {r['kept_pair_fraction']:.2f} of pairs, {r['kernel_ms_avg']:.3f} ms, "
-                f"x{r['speedup_vs_dense_edit1024']:.2f} vs dense")
+            if rule == "bound":
+                sparse_checks[r["workload"]] = (sinp, smask)
+            log(f"{r['workload']}: kept {r['kept_pair_fraction']:.2f} of pairs, mask {r['mask_ms']:.3f} ms, "
+                f"attention {r['kernel_ms_avg']:.3f} ms (x{r['speedup_vs_dense_edit1024']:.2f} vs dense), "
+                f"deviation from dense rel-L2 {r['deviation_from_dense_rel_l2']:.2e}")
 
     traffic = recorded_traffic("attn_bf16", "edit1024")
     achieved = main_run["kernel_tflops"]
@@ -448,7 +480,7 @@ def main():
         "extra": [rnd(r) for r in extra],
     }
     if not args.no_cpu_baseline:
-        base, main_err, out_err = cpu_baseline(main_inp, main_out, checks)
+        base, main_err, out_err = cpu_baseline(main_inp, main_out, checks, sparse_checks)
         line["cpu_baseline"] = base
         line["error_vs_oracle"] = main_err
         for r in line["extra"]:
