@@ -1,14 +1,23 @@
-// Tile-sparse attention support: the pooled-score tile mask and the lists of
-// kept key tiles.
+// Tile-sparse attention support: the tile masks and the lists of kept key
+// tiles.
 //
 // Sparse attention skips the work for less important token pairs according to
 // a sparsity threshold tau ("Optimizing FLUX 3 Image Klein inference on NVIDIA
-// Blackwell GPUs", How it works; What you can do: tau).  The importance
-// measure and granularity are this library's reading: 256-token query tiles x
-// 64-token key tiles; the pooled score of a tile pair is
-// c * <mean of the tile's rotated q, mean of the tile's rotated k>
-// (c = scale * log2 e); a key tile is kept when its pooled score is at least
-// the query tile's largest plus log2(tau).
+// Blackwell GPUs", How it works; What you can do: tau).  Granularity and
+// importance measure are this library's reading: 256-token query tiles x
+// 64-token key tiles, and two rules (c = scale * log2 e, exp2 domain):
+//   score bound (tile_bound_kernel): key tile t is skipped for query tile Q
+//     when, for every query i of Q, i's largest score over t is below
+//     L_i + log2(tau), with L_i i's largest score over the 4 key tiles aligned
+//     with Q (a lower bound of its row maximum); every skipped pair then has
+//     weight below tau times its row's largest, which bounds the distance
+//     from dense attention;
+//   pooled score (tile_mean_kernel, block_select_kernel), an alternative
+//     without that guarantee: the pooled score of a tile pair is
+//     c * <mean of the tile's rotated q, mean of the tile's rotated k>; a key
+//     tile is kept when its pooled score is at least the query tile's largest
+//     plus log2(tau).
+#include "attn_common.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -81,6 +90,115 @@ __global__ __launch_bounds__(256) void block_select_kernel(const float* __restri
   mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float thr = mx + log2_tau;
   for (int kt = threadIdx.x; kt < KT; kt += 256) mask[(size_t)row * KT + kt] = sc[kt] >= thr ? 1 : 0;
+}
+
+// Score-bound rule for one (b, h, 256-row query tile) per workgroup: 8 waves
+// x 32 queries.  Q and K are rotated, scaled and rounded exactly as in the
+// attention kernel (same table, same bf16 operands), the scores are bf16
+// MFMA sums in fp32.  The workgroup first walks the 4 key tiles aligned with
+// its query tile, each query keeping its largest score L, then every key tile
+// t, each wave reducing max over its queries of (tile max - L) into
+// red[wave][t]; at the end red's column maxima decide the mask row.  K tiles
+// are double-buffered in LDS, one barrier per tile.
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void tile_bound_kernel(BoundArgs a) {
+  constexpr int BN = 64, NT = 512, KSTEPS = D / 16, CPR = D / 8, RPP = NT / CPR, NPASS = BN / RPP;
+  constexpr int KTILEB = BN * LdsRows<D>::K;
+  __shared__ __attribute__((aligned(16))) char ksm[2][KTILEB];
+  extern __shared__ float red[];  // [8][KT]
+  const int N = a.n_tokens, H = a.heads, KT = a.kt;
+  const int QT = (N + 255) / 256;
+  const int qt = blockIdx.x % QT, bh = blockIdx.x / QT;
+  const int h = bh % H, b = bh / H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const size_t tok_stride = (size_t)H * D;
+  const uint16_t* qbase = a.q + (size_t)b * a.batch_tokens * tok_stride + (size_t)h * D;
+  const uint16_t* kbase = a.k + (size_t)b * a.batch_tokens * tok_stride + (size_t)h * D;
+
+  // Q fragments of this lane's query, rotated, times c, bf16 (rows past N: 0)
+  const int qrow = qt * 256 + wave * 32 + l32;
+  bf16x8 qf[KSTEPS];
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) {
+    const int ch = 2 * t + g;
+    u32x4 x = {0, 0, 0, 0}, w = {0, 0, 0, 0};
+    if (qrow < N) {
+      x = global_load_b128(qbase + (size_t)qrow * tok_stride + 8 * ch);
+      w = global_load_b128(a.rope + (size_t)qrow * (D / 2) + 4 * ch);
+    }
+    qf[t] = __builtin_bit_cast(bf16x8, rope_chunk_scaled(x, w, a.c));
+  }
+
+  // key tile of position p: the 4 aligned tiles first, then all KT
+  const int t_al0 = 4 * qt, n_al = min(4, KT - t_al0);
+  auto tile_of = [&](int p) { return p < n_al ? t_al0 + p : p - n_al; };
+  const int n_pos = n_al + KT;
+  const int st_chunk = tid % CPR, st_row0 = tid / CPR;
+  u32x4 kraw[NPASS], kcs[NPASS];
+  auto load_k = [&](int kt0) {
+    const int rows = N - kt0;
+    const uint32_t kbytes = rows > 0 ? (uint32_t)((rows - 1) * tok_stride * 2 + 2 * D) : 0u;
+    const uint32_t rbytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 4) : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, kbytes);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rope + (size_t)kt0 * (D / 2), rbytes);
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int r = st_row0 + p * RPP;
+      kraw[p] = buffer_load_b128(rk, (uint32_t)(r * tok_stride * 2 + st_chunk * 16));
+      kcs[p] = buffer_load_b128(rr, (uint32_t)(r * (D / 2) * 4 + st_chunk * 16));
+    }
+  };
+  auto store_k = [&](int buf) {
+    FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+      lds_write_b128(kl + k_off<D>(st_row0 + p * RPP, st_chunk), rope_chunk(kraw[p], kcs[p]));
+  };
+
+  load_k(tile_of(0) * BN);
+  store_k(0);
+  if (n_pos > 1) load_k(tile_of(1) * BN);
+  __syncthreads();
+  float low = -INFINITY;  // L of this lane's query
+  for (int p = 0; p < n_pos; ++p) {
+    const int t = tile_of(p), kt0 = t * BN;
+    const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[p & 1];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = {};
+#pragma unroll
+      for (int tt = 0; tt < KSTEPS; ++tt)
+        s = mfma_bf16(__builtin_bit_cast(bf16x8, lds_read_b128(kl + k_off<D>(32 * kb + l32, 2 * tt + g))), qf[tt], s);
+      // element e of lane l: key 32 kb + 8 (e / 4) + 4 g + e % 4 of the tile
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kt0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+        mx = fmaxf(mx, key < N ? s[e] : -INFINITY);
+      }
+    }
+    mx = fmaxf(mx, swap_halves(mx));  // this query's largest score over the tile
+    if (p + 1 < n_pos) store_k((p + 1) & 1);
+    if (p < n_al) {
+      low = fmaxf(low, mx);
+    } else {
+      float v = qrow < N ? mx - low : -INFINITY;
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+      if (lane == 0) red[wave * KT + t] = v;
+    }
+    if (p + 2 < n_pos) load_k(tile_of(p + 2) * BN);
+    __syncthreads();
+  }
+  uint8_t* mrow = a.mask + (size_t)blockIdx.x * KT;
+  for (int t = tid; t < KT; t += NT) {
+    float m = red[t];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) m = fmaxf(m, red[w * KT + t]);
+    mrow[t] = m >= a.log2_tau ? 1 : 0;
+  }
 }
 
 // Kept key tiles of each mask row, ascending, and their count: one wave per
@@ -195,6 +313,20 @@ hipError_t launch_block_select(const float* qbar, const float* kbar, uint8_t* ma
   else if (head_dim == 64)
     hipLaunchKernelGGL(block_select_kernel<64>, dim3(rows), dim3(256), lds, stream, qbar, kbar, mask, QT, KT, c,
                        log2_tau);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_bound(const BoundArgs& a, int head_dim, hipStream_t stream) {
+  const int QT = (a.n_tokens + 255) / 256;
+  const dim3 grid((unsigned)(a.batch * a.heads * QT));
+  const size_t lds = (size_t)8 * a.kt * sizeof(float);
+  if (lds > kBoundMaxLds) return hipErrorInvalidValue;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(tile_bound_kernel<128>, grid, dim3(512), lds, stream, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(tile_bound_kernel<64>, grid, dim3(512), lds, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -734,6 +734,39 @@ int flux_attn_block_mask(flux_attn_plan* plan, const void* q, const void* k, con
   if (st) return st;
   if (!(tau > 0.0f && tau <= 1.0f)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "tau must be in (0, 1]");
   const flux_attn_config& c = plan->cfg;
+  const int KT = (n + 63) / 64;
+  if ((size_t)8 * KT * sizeof(float) > flux::kBoundMaxLds)
+    return fail(FLUX_ATTN_UNSUPPORTED, "the score-bound tile mask supports at most %zu key tiles (%d tokens); got %d",
+                flux::kBoundMaxLds / 32, (int)(flux::kBoundMaxLds / 32) * 64, KT);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = flux::launch_rope_table(pos_ids, plan->freq, rope16(plan), n, c.head_dim, c.rope_axes_dim[0],
+                                         c.rope_axes_dim[1], stream);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  flux::BoundArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.rope = rope16(plan);
+  a.mask = mask;
+  a.n_tokens = n;
+  a.batch_tokens = n;
+  a.heads = c.num_heads;
+  a.batch = c.batch;
+  a.kt = KT;
+  a.c = plan_c(c);
+  a.log2_tau = std::log2(tau);
+  e = flux::launch_tile_bound(a, c.head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "block mask launch");
+  return ok();
+}
+
+int flux_attn_block_mask_pooled(flux_attn_plan* plan, const void* q, const void* k, const int32_t* segment_tokens,
+                                int32_t num_segments, const int32_t* pos_ids, float tau, uint8_t* mask,
+                                void* hip_stream) {
+  int n = 0;
+  int st = sparse_common(plan, q, k, k, segment_tokens, num_segments, pos_ids, nullptr, mask, &n);
+  if (st) return st;
+  if (!(tau > 0.0f && tau <= 1.0f)) return fail(FLUX_ATTN_INVALID_ARGUMENT, "tau must be in (0, 1]");
+  const flux_attn_config& c = plan->cfg;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   float2* const table = static_cast<float2*>(plan->rope_table);
   hipError_t e = flux::launch_rope_table_f32(pos_ids, plan->freq, table, n, c.head_dim, c.rope_axes_dim[0],

@@ -139,6 +139,27 @@ hipError_t launch_tile_means(const uint16_t* x, const float2* rope, float* out, 
 // threshold row max + log2_tau: uint8 [rows][KT].
 hipError_t launch_block_select(const float* qbar, const float* kbar, uint8_t* mask, int rows, int QT, int KT,
                                int head_dim, float c, float log2_tau, hipStream_t stream);
+// Score-bound tile mask: for each (b, h, query tile) row of mask [B][H][QT][KT],
+// key tile t is kept when max over the tile's queries i of (i's largest score
+// over t - L_i) >= log2_tau, L_i = i's largest score over the 4 key tiles
+// aligned with the query tile (scores c <R q, R k> in the exp2 domain, bf16
+// operands as in the attention kernel).
+struct BoundArgs {
+  const uint16_t* q;      // [B][batch_tokens][H][D] bf16 bits
+  const uint16_t* k;
+  const uint32_t* rope;   // [N][D/2] packed fp16 (cos, sin)
+  uint8_t* mask;          // [B][H][QT][KT]
+  int n_tokens;
+  int batch_tokens;
+  int heads;
+  int batch;
+  int kt;                 // ceil(N / 64)
+  float c;                // scale * log2(e)
+  float log2_tau;
+};
+// Dynamic LDS of the per-wave reductions (8 x KT floats): KT <= 2048.
+constexpr size_t kBoundMaxLds = 64 * 1024;
+hipError_t launch_tile_bound(const BoundArgs& a, int head_dim, hipStream_t stream);
 // Kept key tiles of each mask row (ascending) into list[row * stride + i], count[row].
 hipError_t launch_mask_to_list(const uint8_t* mask, int* list, int* count, int rows, int KT, int stride,
                                hipStream_t stream);

@@ -83,6 +83,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flux_attn_timing_read": ([_vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                    ctypes.POINTER(ctypes.c_double), _i32, _i32p], ctypes.c_int),
         "flux_attn_block_mask": ([_vp, _vp, _vp, _i32p, _i32, _vp, ctypes.c_float, _vp, _vp], ctypes.c_int),
+        "flux_attn_block_mask_pooled": ([_vp, _vp, _vp, _i32p, _i32, _vp, ctypes.c_float, _vp, _vp], ctypes.c_int),
         "flux_attn_forward_sparse": ([_vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
         "flux_attn_forward_lse": ([_vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
         "flux_attn_backward": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32p, _i32, _vp, _vp, _vp, _vp, _vp],
@@ -265,8 +266,13 @@ class Plan:
         c = self.config
         return (c.batch, c.num_heads, (n_tokens + 255) // 256, (n_tokens + 63) // 64)
 
-    def block_mask(self, q, k, segment_tokens: Sequence[int], pos_ids, tau: float, mask=None, stream=None):
-        """Tile mask of the pooled-score rule (uint8 [B, H, QT, KT]) for threshold tau."""
+    def block_mask(self, q, k, segment_tokens: Sequence[int], pos_ids, tau: float, mask=None, stream=None,
+                   rule: str = "bound"):
+        """Tile mask (uint8 [B, H, QT, KT]) for threshold tau: rule "bound"
+        (flux_attn_block_mask, the score-bound rule) or "pooled"
+        (flux_attn_block_mask_pooled)."""
+        if rule not in ("bound", "pooled"):
+            raise FluxAttnError(INVALID_ARGUMENT, f"unknown rule {rule!r}")
         import torch
         n, _ = self._check_qkv(q, k, k, segment_tokens, pos_ids)
         ms = self.mask_shape(n)
@@ -277,9 +283,9 @@ class Plan:
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         segs = _i32_array(segment_tokens)
-        check(self._lib.flux_attn_block_mask(self._handle, q.data_ptr(), k.data_ptr(), segs, len(segment_tokens),
-                                             pos_ids.data_ptr(), float(tau), mask.data_ptr(), stream.cuda_stream),
-              "block_mask")
+        fn = self._lib.flux_attn_block_mask if rule == "bound" else self._lib.flux_attn_block_mask_pooled
+        check(fn(self._handle, q.data_ptr(), k.data_ptr(), segs, len(segment_tokens), pos_ids.data_ptr(),
+                 float(tau), mask.data_ptr(), stream.cuda_stream), f"block_mask ({rule})")
         return mask
 
     def forward_sparse(self, q, k, v, segment_tokens: Sequence[int], pos_ids, mask, out=None, stream=None):

@@ -196,14 +196,31 @@ int flux_attn_backward(flux_attn_plan* plan, const void* q, const void* k, const
  * asynchronously on hip_stream and share the plan's workspace (one call at a
  * time per plan). */
 
-/* Writes the mask of the pooled-score rule: the pooled score of a tile pair is
- * scale * log2(e) * <mean over the query tile of R(p_i) q_i, mean over the key
- * tile of R(p_j) k_j> (fp32); a key tile is kept when its pooled score is at
- * least the query tile's largest plus log2(tau), 0 < tau <= 1, so the largest
- * is always kept.  mask is written in full. */
+/* Writes the mask of the score-bound rule (scores s_ij = scale * log2(e) *
+ * <R(p_i) q_i, R(p_j) k_j>, exp2 domain, from the same bf16 operands and
+ * fp32 accumulation as the attention kernel): with L_i the largest score of
+ * query i over the 4 key tiles aligned with its query tile (a lower bound of
+ * its row maximum m_i), key tile t is kept for query tile Q when
+ *     max over i in Q of ( max over j in t of s_ij  -  L_i )  >=  log2(tau),
+ * 0 < tau <= 1.  Every skipped pair then has weight 2^(s_ij - m_i) < tau
+ * relative to its row's largest, and the output moves from dense attention by
+ * at most delta_i (max_j V[j,d] - min_j V[j,d]) per element, delta_i (the
+ * dense softmax mass of row i's skipped keys) being below tau times the
+ * number of skipped keys.  Its cost is one pass of Q K^T over all tiles.
+ * N <= 131,072 (FLUX_ATTN_UNSUPPORTED beyond).  mask is written in full. */
 int flux_attn_block_mask(flux_attn_plan* plan, const void* q, const void* k, const int32_t* segment_tokens,
                          int32_t num_segments, const int32_t* pos_ids, float tau, uint8_t* mask,
                          void* hip_stream);
+
+/* Alternative rule without that guarantee, cheaper (tile means only): the
+ * pooled score of a tile pair is scale * log2(e) * <mean over the query tile
+ * of R(p_i) q_i, mean over the key tile of R(p_j) k_j> (fp32); a key tile is
+ * kept when its pooled score is at least the query tile's largest plus
+ * log2(tau), 0 < tau <= 1, so the largest is always kept.  mask is written in
+ * full. */
+int flux_attn_block_mask_pooled(flux_attn_plan* plan, const void* q, const void* k,
+                                const int32_t* segment_tokens, int32_t num_segments, const int32_t* pos_ids,
+                                float tau, uint8_t* mask, void* hip_stream);
 
 /* Attention of each query over the keys of its query tile's kept key tiles:
  * the exact softmax over those keys (the others are left out); a query tile

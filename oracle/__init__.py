@@ -12,8 +12,10 @@ What it computes (every function cites the passage it follows):
                      blocked over query rows, fp64;
   * ``e4m3``       - decoding of OCP 8-bit e4m3 ("e4m3fn") codes from the
                      format's definition;
-  * ``block_sparse`` - the tile-mask rule of threshold-sparse attention and
-                     exact attention over the kept tiles;
+  * ``block_sparse`` - the tile-mask rules of threshold-sparse attention (the
+                     score-bound rule with its error bound against dense
+                     attention, and the pooled-score rule) and exact
+                     attention over the kept tiles;
   * ``backward``   - gradients (dq, dk, dv) of joint RoPE attention and the
                      per-row log-sum-exp.
 
@@ -28,5 +30,6 @@ from .softmax_attention import (softmax_rows, attention_from_scores, attention, 
                         segment_local_rope_attention)
 from .e4m3 import e4m3_decode, e4m3_table, dequantize  # noqa: F401
 from .inputs_fp64 import inputs_to_fp64  # noqa: F401
-from .block_sparse import tile_means, block_scores, block_mask, block_sparse_attention  # noqa: F401
+from .block_sparse import (tile_means, block_scores, block_mask, block_sparse_attention,  # noqa: F401
+                           tile_score_maxima, bound_mask, skipped_mass, skip_mass_bound, dense_error_bound)
 from .backward import rope_transpose, attention_lse, attention_backward  # noqa: F401

@@ -1,11 +1,15 @@
-"""GPU parity of tile-sparse attention and of its tile-mask rule.
+"""GPU parity of tile-sparse attention and of its tile-mask rules.
 
 forward_sparse is compared with the oracle's exact attention over the same
 kept tiles (oracle/block_sparse.py); the masks are drawn by seeded random
-generators here or computed by the oracle's rule, never taken from the GPU.
-The GPU mask rule is compared with the oracle's rule wherever the decision is
-clear (|margin| > 1e-3 in the exp2 domain); closer decisions may go either way
-in fp32 and are only checked to be 0/1.
+generators here, computed by the oracle's rules, or (where the GPU rule's own
+output is what is being tested) checked against the oracle's margins.  The GPU
+mask rules are compared with the oracle's wherever the decision is clear:
+|margin| > 1e-3 (exp2 domain) for the pooled rule, whose pooled scores are
+fp32 sums; |margin| > 0.5 for the score-bound rule, whose scores are bf16 MFMA
+sums of bf16-rounded rotated operands (up to ~2^-8 relative each, scores of
+up to ~40 on these inputs).  Closer decisions may go either way and are only
+checked to be 0/1.
 """
 import numpy as np
 import pytest
@@ -81,10 +85,12 @@ def test_all_kept_equals_dense_bitwise(monkeypatch):
 
 
 def test_edit1024_local_oracle_mask_sampled_rows():
-    # sigma 1.5 with a shared Q/K direction: scores span tens of units, rows are
-    # peaked, and the bf16 error of the dense kernel itself is near the 5e-3
-    # bound (like the sigma = 2 stress case).  The sparse path must be as
-    # accurate as the dense kernel on the same inputs and rows.
+    # sigma 1.5 with a shared Q/K direction: scores span tens of units and rows
+    # are peaked.  The workloads' bound (relative L2 5e-3) is stated for
+    # sigma <= 1 inputs; here the bf16 rounding of the rotated operands moves
+    # scores of ~30 (exp2 domain) by up to ~0.1, and the dense kernel itself
+    # measures about 5.3e-3, so this input is held to 7.5e-3 (1.5x) and the
+    # sparse path to the dense kernel's own accuracy on the same rows.
     from gpu_helpers import errors, ref_rows, run_hip
     w = I.WORKLOADS["edit1024_local"]
     inp = I.make_inputs(w)
@@ -98,23 +104,27 @@ def test_edit1024_local_oracle_mask_sampled_rows():
     say(f"  edit1024_local tau 0.01, kept {mask.mean():.2f}: sparse max-abs {ma:.3e} rel-L2 {rl:.3e}; "
         f"dense max-abs {dma:.3e} rel-L2 {drl:.3e}")
     assert rl <= 1.2 * drl + 1e-4 and ma <= 2.0 * dma + 1e-3
-    assert rl <= 1e-2
+    assert drl <= 7.5e-3 and rl <= 7.5e-3
+
+
+def _mask_workload(name):
+    if name == "sp_small":
+        w = custom("sp_small", 3, 128, [S("text", 200), S("image", 30, 30)], sigma=1.5)
+        return I.Workload(w.name, w.batch, w.heads, w.head_dim, w.segments, w.sigma, w.fp8, w.seed,
+                          w.description, 0.9)
+    return I.WORKLOADS[name]
 
 
 @pytest.mark.parametrize("name,tau", [("edit1024_local", 0.01), ("edit1024_local", 0.1), ("sp_small", 0.3)])
-def test_block_mask_matches_oracle_rule(name, tau):
+def test_pooled_mask_matches_oracle_rule(name, tau):
     import torch
-    if name == "sp_small":
-        w = custom("sp_small", 3, 128, [S("text", 200), S("image", 30, 30)], sigma=1.5)
-        w = I.Workload(w.name, w.batch, w.heads, w.head_dim, w.segments, w.sigma, w.fp8, w.seed, w.description, 0.9)
-    else:
-        w = I.WORKLOADS[name]
+    w = _mask_workload(name)
     inp = I.make_inputs(w)
     q, k, v = oracle.inputs_to_fp64(inp)
     want, margin = oracle.block_mask(oracle.block_scores(q, k, inp.pos, w.axes_dim), tau)
     qd, kd, _, pos, _ = to_device(inp)
     with _plan(w) as plan:
-        got = plan.block_mask(qd, kd, inp.segment_tokens, pos, tau)
+        got = plan.block_mask(qd, kd, inp.segment_tokens, pos, tau, rule="pooled")
         torch.cuda.synchronize()
     got = got.cpu().numpy()
     assert set(np.unique(got)) <= {0, 1}
@@ -122,3 +132,63 @@ def test_block_mask_matches_oracle_rule(name, tau):
     say(f"  {name} tau {tau}: kept {want.mean():.3f}, unclear decisions {int((~clear).sum())} of {clear.size}")
     assert np.array_equal(got.astype(bool)[clear], want[clear])
     assert got.sum(axis=-1).min() >= 1
+
+
+@pytest.mark.parametrize("name,tau", [("edit1024_local", 0.1), ("edit1024_local", 0.01), ("sp_small", 0.3),
+                                      ("sp_small", 0.03)])
+def test_bound_mask_matches_oracle_rule(name, tau):
+    import time
+    import torch
+    w = _mask_workload(name)
+    inp = I.make_inputs(w)
+    q, k, v = oracle.inputs_to_fp64(inp)
+    t0 = time.perf_counter()
+    smax, m = oracle.tile_score_maxima(q, k, inp.pos, w.axes_dim)
+    want, margin = oracle.bound_mask(smax, tau)
+    say(f"  oracle tile maxima: {time.perf_counter() - t0:.1f} s")
+    qd, kd, _, pos, _ = to_device(inp)
+    with _plan(w) as plan:
+        say(f"  HIP block_mask (bound): {w.name} N={w.tokens} H={w.heads} tau {tau}")
+        got = plan.block_mask(qd, kd, inp.segment_tokens, pos, tau)
+        torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert set(np.unique(got)) <= {0, 1}
+    clear = np.abs(margin - np.log2(tau)) > 0.5
+    say(f"  {name} tau {tau}: oracle keeps {want.mean():.3f}, GPU {got.mean():.3f}; "
+        f"unclear decisions {int((~clear).sum())} of {clear.size}")
+    assert np.array_equal(got.astype(bool)[clear], want[clear])
+    assert (~clear).mean() < 0.05
+    # every query keeps its best aligned tile, so no row is left without keys
+    assert got.sum(axis=-1).min() >= 1
+
+
+def test_bound_mask_sparse_attention_and_dense_error_bound():
+    # The GPU's own score-bound mask at tau 0.1 on the position-local input:
+    # forward_sparse against the oracle's attention over the same kept tiles,
+    # and the oracle's dense attention within the proven distance
+    # delta_i (max V - min V) of that sparse result (delta_i: dense softmax mass
+    # of row i's skipped keys), on sampled rows.
+    import torch
+    from gpu_helpers import errors, ref_rows
+    w = I.WORKLOADS["edit1024_local"]
+    inp = I.make_inputs(w)
+    qd, kd, _, pos, _ = to_device(inp)
+    with _plan(w) as plan:
+        m = plan.block_mask(qd, kd, inp.segment_tokens, pos, 0.1)
+        torch.cuda.synchronize()
+    mask = m.cpu().numpy().astype(bool)
+    say(f"  GPU bound mask keeps {mask.mean():.3f} of tiles")
+    assert (~mask).any()
+    got = out_fp64(_run_sparse(inp, mask))
+    rows = sample_rows(w.tokens, seed=12, count=40)
+    sp_ref = _oracle(inp, mask, rows=rows)
+    ma, rl = errors(got[:, rows], sp_ref)
+    say(f"  sparse vs oracle sparse: max-abs {ma:.3e} rel-L2 {rl:.3e}")
+    assert rl <= 7.5e-3 and ma <= 2e-2
+    q, k, v = oracle.inputs_to_fp64(inp)
+    dense = ref_rows(inp, rows)
+    delta = oracle.skipped_mass(q, k, inp.pos, w.axes_dim, mask)        # [B, H, N]
+    bound = oracle.dense_error_bound(delta, v)[:, rows]
+    dev = np.abs(sp_ref - dense)
+    say(f"  oracle sparse vs dense: max {dev.max():.3e}, bound max {bound.max():.3e}, max delta {delta.max():.3e}")
+    assert (dev <= bound + 1e-12).all()

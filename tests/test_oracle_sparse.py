@@ -153,3 +153,134 @@ def test_mutations_are_caught():
     m_good, _ = obs.block_mask(s, 0.3)
     m_wrong_sign = s <= s.max(axis=-1, keepdims=True) + math.log2(0.3)
     assert (m_good != m_wrong_sign).any()
+
+
+# ----------------------------------------------------------------------------------
+# score-bound rule: guarantee and error bound against dense attention
+
+def _peaked(n=72, h=2, seed=30, sigma=3.0, a=0.95):
+    """Q and K sharing a per-head direction, positions along one axis: with
+    RoPE the scores peak near equal positions, so far tiles can be skipped."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((1, 1, h, 32))
+    b = math.sqrt(1 - a * a)
+    q = sigma * (a * u + b * rng.standard_normal((1, n, h, 32)))
+    k = sigma * (a * u + b * rng.standard_normal((1, n, h, 32)))
+    v = rng.standard_normal((1, n, h, 32))
+    pos = np.zeros((n, 3), np.int32)
+    pos[:, 2] = np.arange(n)
+    return q, k, v, pos
+
+
+def _scores_loop(q, k, pos, b, h):
+    """exp2-domain scores by explicit loops over a rotation written as 2x2 matrices."""
+    n, D = q.shape[1], q.shape[3]
+    freqs = []
+    for d in AXES:
+        freqs += [10000.0 ** (-2.0 * j / d) for j in range(d // 2)]
+    axis = [a for a, d in enumerate(AXES) for _ in range(d // 2)]
+    def rot(x, p):
+        out = np.empty(D)
+        for j in range(D // 2):
+            ang = p[axis[j]] * freqs[j]
+            cs, sn = math.cos(ang), math.sin(ang)
+            out[2 * j] = cs * x[2 * j] - sn * x[2 * j + 1]
+            out[2 * j + 1] = sn * x[2 * j] + cs * x[2 * j + 1]
+        return out
+    qr = [rot(q[b, i, h], pos[i]) for i in range(n)]
+    kr = [rot(k[b, j, h], pos[j]) for j in range(n)]
+    c = 1.0 / math.sqrt(D) / math.log(2.0)
+    return np.array([[c * float(np.dot(qr[i], kr[j])) for j in range(n)] for i in range(n)])
+
+
+def test_bound_rule_brute_force():
+    q, k, v, pos = _peaked()
+    n, qs, ks = q.shape[1], 16, 4
+    smax, m = obs.tile_score_maxima(q, k, pos, AXES, k_tile=ks)
+    mask, margin = obs.bound_mask(smax, 0.1, q_tile=qs, k_tile=ks)
+    for h in range(2):
+        s = _scores_loop(q, k, pos, 0, h)
+        for qt in range((n + qs - 1) // qs):
+            rows = range(qt * qs, min(n, (qt + 1) * qs))
+            own = range(qt * qs // ks, min((n + ks - 1) // ks, (qt + 1) * qs // ks))
+            low = {i: max(s[i, j] for t in own for j in range(t * ks, min(n, (t + 1) * ks))) for i in rows}
+            for t in range((n + ks - 1) // ks):
+                keys = range(t * ks, min(n, (t + 1) * ks))
+                want = max(s[i, j] - low[i] for i in rows for j in keys)
+                assert abs(margin[0, h, qt, t] - want) < 1e-9
+                assert mask[0, h, qt, t] == (want >= math.log2(0.1))
+        np.testing.assert_allclose(m[0, h], s.max(axis=1), rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("tau", [0.3, 0.1, 0.01])
+def test_bound_rule_guarantee_and_dense_error_bound(tau):
+    q, k, v, pos = _peaked()
+    n, qs, ks = q.shape[1], 16, 4
+    smax, m = obs.tile_score_maxima(q, k, pos, AXES, k_tile=ks)
+    mask, _ = obs.bound_mask(smax, tau, q_tile=qs, k_tile=ks)
+    per = qs // ks
+    for qt in range(mask.shape[2]):                      # every query keeps its best aligned tile
+        best = qt * per + smax[:, :, qt * qs:(qt + 1) * qs, qt * per:(qt + 1) * per].argmax(axis=-1)
+        for h in range(2):
+            assert mask[0, h, qt, best[0, h]].all()
+    keep = obs._expand_mask(mask, n, qs, ks)
+    if tau <= 0.1:
+        assert (~mask).mean() > 0.2                      # the rule does skip tiles here
+    deltas = obs.skipped_mass(q, k, pos, AXES, mask, q_tile=qs, k_tile=ks)
+    for h in range(2):
+        s = _scores_loop(q, k, pos, 0, h)
+        rel = np.exp2(s - s.max(axis=1, keepdims=True))  # weight relative to the row's largest
+        assert (rel[~keep[0, h]] < tau).all()            # the guarantee, pair by pair
+        p = rel / rel.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(deltas[0, h], (p * ~keep[0, h]).sum(axis=1), rtol=1e-12, atol=1e-15)
+    nk = np.array([min(ks, n - t * ks) for t in range(mask.shape[3])])
+    bound = obs.skip_mass_bound(smax, m, mask, nk, q_tile=qs)
+    skipped_keys = (~keep).sum(axis=-1)
+    assert (deltas <= bound * (1 + 1e-12)).all()
+    assert (bound <= tau * skipped_keys + 1e-15).all()
+    dense = oracle.joint_rope_attention(q, k, v, pos, AXES)
+    sparse = obs.block_sparse_attention(q, k, v, pos, AXES, mask, q_tile=qs, k_tile=ks)
+    eb = obs.dense_error_bound(deltas, v)
+    assert (np.abs(sparse - dense) <= eb + 1e-13).all()
+    # the bound is attained up to the spread of V: not vacuous
+    if tau <= 0.1:
+        assert np.abs(sparse - dense).max() > 0.05 * eb.max()
+
+
+def test_bound_rule_tau_extremes():
+    q, k, v, pos = _peaked()
+    smax, _ = obs.tile_score_maxima(q, k, pos, AXES, k_tile=4)
+    m1, mg = obs.bound_mask(smax, 1.0, q_tile=16, k_tile=4)
+    assert (m1 == (mg >= 0.0)).all()
+    m0, _ = obs.bound_mask(smax, 1e-300, q_tile=16, k_tile=4)
+    assert m0.all()
+    with pytest.raises(ValueError):
+        obs.bound_mask(smax, 0.0)
+
+
+def test_bound_rule_mutations_break_the_guarantee():
+    # plausible mistakes in the rule: the smallest row instead of the largest
+    # deciding a tile, or the lower bound taken from the whole row's minimum
+    # tile; each must skip some pair whose weight reaches tau
+    q, k, v, pos = _peaked()
+    n, qs, ks, tau = q.shape[1], 16, 4, 0.1
+    smax, m = obs.tile_score_maxima(q, k, pos, AXES, k_tile=ks)
+    s = [_scores_loop(q, k, pos, 0, h) for h in range(2)]
+
+    def violates(mask):
+        keep = obs._expand_mask(mask, n, qs, ks)
+        return any((np.exp2(s[h] - s[h].max(axis=1, keepdims=True))[~keep[0, h]] >= tau).any() for h in range(2))
+
+    good, _ = obs.bound_mask(smax, tau, q_tile=qs, k_tile=ks)
+    assert not violates(good)
+    per = qs // ks
+    bad_rows = np.empty_like(good)
+    bad_low = np.empty_like(good)
+    for qt in range(good.shape[2]):
+        blk = smax[:, :, qt * qs:(qt + 1) * qs]
+        low = blk[..., qt * per:(qt + 1) * per].max(axis=-1, keepdims=True)
+        bad_rows[:, :, qt] = (blk - low).min(axis=2) >= math.log2(tau)
+        bad_low[:, :, qt] = (blk - blk.max(axis=-1, keepdims=True)).max(axis=2) + 0.0 >= \
+            math.log2(tau) + (blk.max(axis=-1) - blk.min(axis=-1)).mean(axis=2)[..., None]
+    assert violates(bad_rows)
+    assert violates(bad_low)
