@@ -601,99 +601,6 @@ void attn_fwd_bf16_persistent_kernel(AttnArgs a) {
   probe.finish();
 }
 
-// Merge of a persistent-split launch: block (c - 1) * 16 + sub, for each
-// slice boundary c in [1, gridDim/16], takes rows 16 sub .. 16 sub + 15 of
-// the tile that the boundary cuts (if it is the first boundary inside it),
-// 16 threads per row, 8 dims each, and combines the partials of the slices
-// that cover the tile.
-template <int D>
-__global__ __launch_bounds__(256) void attn_merge_sk_kernel(AttnArgs a) {
-  const int ncu = a.sk_cus, nkv = a.sk_nkv;
-  const long W = (long)a.sk_tiles * nkv;
-  const int c = blockIdx.x / 16 + 1, sub = blockIdx.x % 16;
-  const long bc = W * c / ncu;
-  if (bc % nkv == 0) return;  // the boundary falls between tiles
-  const int T = (int)(bc / nkv);
-  const long t_start = (long)T * nkv, t_end = t_start + nkv;
-  if (c > 1 && W * (c - 1) / ncu > t_start) return;  // an earlier boundary cuts T
-  const int r = sub * 16 + (threadIdx.x >> 4), d0 = (threadIdx.x & 15) * 8;
-  const int N = a.rng_len[0];
-  const int q_tiles = (N + 255) / 256;
-  const int qt = T % q_tiles, bh = T / q_tiles;
-  const int h = bh % a.heads, b = bh / a.heads;
-  const int row = qt * 256 + r;
-  if (row >= N) return;
-  // slices c - 1 .. c_last cover T; slice c' keeps T's piece in slot 2c' when
-  // T is its first tile, else 2c' + 1
-  auto slot_of = [&](int cc) { return 2 * cc + ((W * cc / ncu) / nkv == T ? 0 : 1); };
-  float m = -INFINITY;
-  auto empty = [&](int cc) { return W * (cc + 1) / ncu == W * cc / ncu; };
-  for (int cc = c - 1; cc < ncu && W * cc / ncu < t_end; ++cc)
-    if (!empty(cc)) m = fmaxf(m, a.part_ml[(size_t)slot_of(cc) * 256 + r].x);
-  float l = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int cc = c - 1; cc < ncu && W * cc / ncu < t_end; ++cc) {
-    if (empty(cc)) continue;
-    const int sl = slot_of(cc);
-    const float2 ml = a.part_ml[(size_t)sl * 256 + r];
-    const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - m) : 0.f;
-    l += w * ml.y;
-    const float* po = a.part_o + ((size_t)sl * 256 + r) * D + d0;
-    const f32x4 x0 = *(const f32x4*)po, x1 = *(const f32x4*)(po + 4);
-    acc[0] += w * x0[0]; acc[1] += w * x0[1]; acc[2] += w * x0[2]; acc[3] += w * x0[3];
-    acc[4] += w * x1[0]; acc[5] += w * x1[1]; acc[6] += w * x1[2]; acc[7] += w * x1[3];
-  }
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  if (a.lse != nullptr && d0 == 0)
-    a.lse[((size_t)b * a.heads + h) * N + row] = (m + __builtin_log2f(l)) * 0.6931471805599453f;
-  u32x4 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
-  const size_t tok_stride = (size_t)a.heads * D;
-  *(u32x4*)(a.o + ((size_t)b * a.batch_tokens + a.rng_tok0[0] + row) * tok_stride + (size_t)h * D + d0) = out;
-}
-
-// One thread per (split tile, row, 8 output dims): combines the `split`
-// partial states of its row exactly and writes bf16.
-template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const int per_tile = 256 * (D / 8);
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const int st = idx / per_tile;
-  const int rem = idx - st * per_tile;
-  const int r = rem / (D / 8), d0 = (rem % (D / 8)) * 8;
-  const int tile_g = a.tile_order != nullptr ? a.tile_order[a.whole + st] : a.whole + st;
-  int rg = 0;
-  while (rg + 1 < a.nranges && tile_g >= a.rng_tile0[rg + 1]) ++rg;
-  const int N = a.rng_len[rg], tok0 = a.rng_tok0[rg];
-  const int tile = tile_g - a.rng_tile0[rg];
-  const int q_tiles = (N + 255) / 256;
-  const int qt = tile % q_tiles, bh = tile / q_tiles;
-  const int h = bh % a.heads, b = bh / a.heads;
-  const int row = qt * 256 + r;
-  if (row >= N) return;
-  const int slot0 = st * a.split;
-  float m = -INFINITY;
-  for (int i = 0; i < a.split; ++i) m = fmaxf(m, a.part_ml[(size_t)(slot0 + i) * 256 + r].x);
-  float l = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int i = 0; i < a.split; ++i) {
-    const float2 ml = a.part_ml[(size_t)(slot0 + i) * 256 + r];
-    const float w = ml.y > 0.f ? __builtin_amdgcn_exp2f(ml.x - m) : 0.f;  // empty ranges weigh 0
-    l += w * ml.y;
-    const float* po = a.part_o + ((size_t)(slot0 + i) * 256 + r) * D + d0;
-    const f32x4 x0 = *(const f32x4*)po, x1 = *(const f32x4*)(po + 4);
-    acc[0] += w * x0[0]; acc[1] += w * x0[1]; acc[2] += w * x0[2]; acc[3] += w * x0[3];
-    acc[4] += w * x1[0]; acc[5] += w * x1[1]; acc[6] += w * x1[2]; acc[7] += w * x1[3];
-  }
-  const float inv = l > 0.f ? 1.0f / l : 0.f;  // 0: no kept keys (tile-sparse)
-  if (a.lse != nullptr && d0 == 0)
-    a.lse[((size_t)b * a.heads + h) * N + row] = (m + __builtin_log2f(l)) * 0.6931471805599453f;
-  u32x4 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = pack_bf16(acc[2 * i] * inv, acc[2 * i + 1] * inv);
-  const size_t tok_stride = (size_t)a.heads * D;
-  *(u32x4*)(a.o + ((size_t)b * a.batch_tokens + tok0 + row) * tok_stride + (size_t)h * D + d0) = out;
-}
-
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream) {
   AttnArgs args = a;
   args.whole = sch.whole_tiles;
@@ -719,37 +626,6 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, const Schedule& sch
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), dim3(sch.grid), dim3(Bf16Cfg<64>::NT), 0, stream, args);
   else if (head_dim == 64)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), dim3(sch.grid), dim3(Bf16Cfg<64>::NT), 0, stream, args);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, const Schedule& sch, hipStream_t stream) {
-  if (sch.sk_nkv > 0) {
-    AttnArgs args = a;
-    args.sk_nkv = sch.sk_nkv;
-    args.sk_tiles = sch.sk_tiles;
-    args.sk_cus = sch.sk_cus;
-    const dim3 grid((unsigned)(16 * (sch.sk_cus - 1)));
-    if (sch.sk_cus < 2) return hipSuccess;
-    if (head_dim == 128)
-      hipLaunchKernelGGL(attn_merge_sk_kernel<128>, grid, dim3(256), 0, stream, args);
-    else if (head_dim == 64)
-      hipLaunchKernelGGL(attn_merge_sk_kernel<64>, grid, dim3(256), 0, stream, args);
-    else
-      return hipErrorInvalidValue;
-    return hipGetLastError();
-  }
-  if (sch.split_tiles == 0) return hipSuccess;
-  AttnArgs args = a;
-  args.whole = sch.whole_tiles;
-  args.split = sch.split;
-  const int threads = sch.split_tiles * 256 * (head_dim / 8);
-  const int blocks = (threads + 255) / 256;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(blocks), dim3(256), 0, stream, args);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(blocks), dim3(256), 0, stream, args);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

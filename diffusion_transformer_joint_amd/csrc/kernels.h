@@ -99,7 +99,7 @@ struct RopeFreq {
 // packed fp16 (cos in the low half).
 hipError_t launch_rope_table(const int32_t* pos, const RopeFreq& freq, uint32_t* table, int n_tokens,
                              int head_dim, int d0, int d1, hipStream_t stream);
-// The same angles as fp32 (cos, sin) pairs, for the tile-mask rule.
+// The same angles as fp32 (cos, sin) pairs, for the pooled tile-mask rule.
 hipError_t launch_rope_table_f32(const int32_t* pos, const RopeFreq& freq, float2* table, int n_tokens,
                                  int head_dim, int d0, int d1, hipStream_t stream);
 
