@@ -137,13 +137,17 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
     kv_off[p] = (uint32_t)(r * tok_stride * 2 + st_chunk * 16);
     rp_off[p] = (uint32_t)(r * (D / 2) * 4 + st_chunk * 16);
   }
+  // Range of a resource starting at row kt0: whole token rows up to the end
+  // of the range.  Row r of a tile sits at byte r * tok_stride * 2 (+ its
+  // chunk offset, below 2D), so the rows from N on fall outside the range
+  // and rows before it inside.  Branch-free (max, multiply): a branch here
+  // would split the loop body into several blocks, and the per-slot order
+  // fixed by the scheduling barriers only holds within a block.
   auto tile_bytes = [&](int kt0) -> uint32_t {
-    const int rows = N - kt0;
-    return rows > 0 ? (uint32_t)((rows - 1) * tok_stride * 2 + 2 * D) : 0u;
+    return (uint32_t)max(N - kt0, 0) * (uint32_t)(tok_stride * 2);
   };
   auto load_k = [&](int kt0) {
-    const int rows = N - kt0;
-    const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 4) : 0u;
+    const uint32_t rp_bytes = (uint32_t)max(N - kt0, 0) * (uint32_t)(D / 2 * 4);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, tile_bytes(kt0));
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(rope + (size_t)kt0 * (D / 2), rp_bytes);
 #pragma unroll
@@ -462,6 +466,10 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, char (&ksm)[2][Bf16C
           }
         }
       }
+      // Within the slot: its MFMA first, then its VALU work, so that the
+      // VALU issues while the MFMA runs.
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
       __builtin_amdgcn_sched_barrier(0);
     });
 #pragma unroll

@@ -357,24 +357,28 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
       } else if constexpr (j >= NK && vn < NV) {
         fv[vn % NPF] = vfrag(vn);
       }
-      // staging: RoPE of K(t+1) one dword per slot, then its store; V(t)
-      // widened and stored; loads of K(t+2) and V(t+1)
-      constexpr int R0 = NK;  // first staging slot
-      if constexpr (j >= R0 && j < R0 + 4) {
+      // staging: RoPE of K(t+1), one dword of codes per slot, beside the
+      // 64-cycle score MFMAs (K(t+1) goes to the buffer K(t-1) held, which
+      // is no longer read), then its store; V(t) widened and stored beside
+      // the first output MFMA; loads of K(t+2) and V(t+1) behind them.
+      constexpr int RS = 4;                  // dwords of codes per staged chunk
+      constexpr int R0 = NK >= RS ? 0 : NK;  // first staging slot
+      if constexpr (j >= R0 && j < R0 + RS) {
         if (st_on) ky[j - R0] = rope_dword_e4m3(kraw[j - R0], kcs[(j - R0) >> 1][2 * ((j - R0) & 1)], kcs[(j - R0) >> 1][2 * ((j - R0) & 1) + 1]);
-        if constexpr (j == R0 + 3) {
+        if constexpr (j == R0 + RS - 1) {
           if (st_on) lds_write_b128(kw + st_row * C::K8ROW + st_c * 16, ky);
         }
       }
-      if constexpr (j == R0 + 4) {
+      constexpr int RV = NK > R0 + RS ? NK : R0 + RS;  // V(t) staging slot
+      if constexpr (j == RV) {
         if (st_on) {
           e4m3x16_to_bf16(vraw, &vlo, &vhi);
           lds_write_b128(vw + v_off<D>(st_row, 2 * st_c), vlo);
           lds_write_b128(vw + v_off<D>(st_row, 2 * st_c + 1), vhi);
         }
       }
-      if constexpr (j == R0 + 5) stage_load_k((t + 2) * C::BN);
-      if constexpr (j == R0 + 6) stage_load_v((t + 1) * C::BN);
+      if constexpr (j == RV + 1) stage_load_k((t + 2) * C::BN);
+      if constexpr (j == RV + 2) stage_load_v((t + 1) * C::BN);
       if constexpr (j >= NK) {
         constexpr int v = j - NK;
         if (LAST && v == 0) mask(kt0, 0, s0);
@@ -390,6 +394,10 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
           }
         }
       }
+      // Within the slot: its MFMA first, then its VALU work, so that the
+      // VALU issues while the MFMA runs.
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
       __builtin_amdgcn_sched_barrier(0);
     });
 #pragma unroll
