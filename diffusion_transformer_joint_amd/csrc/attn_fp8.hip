@@ -7,8 +7,9 @@
 // dequantized inputs (codes x scale), bf16 out.
 //
 // Where quantization happens (the pages do not say): the rotary embedding is
-// part of this path, so Q and K are rotated here.  Codes are widened to fp32,
-// rotated, halved and rounded back to e4m3; rotation is linear, so the scales
+// part of this path, so Q and K are rotated here.  Codes are widened to fp16
+// (exactly), rotated with packed fp16 arithmetic, halved and rounded back to
+// e4m3; rotation is linear, so the scales
 // never enter the loop (a rotated pair component is at most sqrt(2) times the
 // pair's largest code, so halving keeps it under 448).  Scores are fp8 MFMA
 // sums of those codes times 4 * s_q * s_k.  P stays bf16 (e4m3 P costs ~2%
@@ -26,8 +27,8 @@
 
 namespace flux {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct Fp8Cfg {
@@ -43,34 +44,30 @@ struct Fp8Cfg {
   static constexpr int VTILEB = BN * (2 * D + 64);  // V tile as bf16, rows as in the bf16 kernel
 };
 
-// Four e4m3 codes (one dword) to floats.
-__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  f[0] = lo[0];
-  f[1] = lo[1];
-  f[2] = hi[0];
-  f[3] = hi[1];
+// One pair of codes widened to fp16, p = (x0, x1), rotated by its table
+// entry cs = (cos, sin): x0 (cos, sin) + x1 (-sin, cos), as packed fp16
+// products (the swap and the sign are operand modifiers).  Every e4m3 value
+// and every rotated value (|y| <= 448 sqrt 2) is an fp16 normal number; the
+// fp16 product and sum round at 2^-11, far below the e4m3 rounding (2^-4)
+// that follows.
+__device__ __forceinline__ f16x2 rot_pair_f16(f16x2 p, f16x2 cs) {
+  const f16x2 sc = {-cs[1], cs[0]};
+  const f16x2 a = {p[0], p[0]}, b = {p[1], p[1]};
+  return __builtin_elementwise_fma(a, cs, b * sc);
 }
 
-// Four floats divided by 2 to e4m3 codes (one dword), round to nearest even.
-// The gfx950 scaled conversion divides by its scale operand before rounding,
-// so the halving costs no instruction; for every input it gives the codes of
-// v_cvt_pk_fp8_f32 on the halved values (checked bitwise on the GPU).
-__device__ __forceinline__ uint32_t f32x4_half_to_e4m3(float a, float b, float c, float d) {
-  s16x2 w = {0, 0};
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, 2.0f, false);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, 2.0f, true);
-  return __builtin_bit_cast(uint32_t, w);
-}
-
-// One dword of codes (two pairs) rotated by table entries w0, w1 and halved.
+// One dword of codes (two pairs) rotated by table entries w0, w1 and halved
+// back to e4m3: one exact widening per pair, two packed fp16 operations per
+// pair, one scaled conversion per pair (scale 2: the halving costs nothing).
 __device__ __forceinline__ uint32_t rope_dword_e4m3(uint32_t x, uint32_t w0, uint32_t w1) {
-  float f[4], y[4];
-  e4m3x4_to_f32(x, f);
-  rot_pair(f[0], f[1], w0, y[0], y[1]);
-  rot_pair(f[2], f[3], w1, y[2], y[3]);
-  return f32x4_half_to_e4m3(y[0], y[1], y[2], y[3]);
+  const f16x2 y0 = rot_pair_f16(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)x, 1.0f, false),
+                                __builtin_bit_cast(f16x2, w0));
+  const f16x2 y1 = rot_pair_f16(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)x, 1.0f, true),
+                                __builtin_bit_cast(f16x2, w1));
+  s16x2 r = __builtin_bit_cast(s16x2, x);  // both halves are overwritten
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, y0, 2.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, y1, 2.0f, true);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // The 8 pairs of 16 codes x (dword-packed) rotated by their table entries
