@@ -7,17 +7,14 @@
 // dequantized inputs (codes x scale), bf16 out.
 //
 // Where quantization happens (the pages do not say): the rotary embedding is
-// part of this path, so Q and K are rotated here.  K codes are widened to
-// fp16 (exactly), rotated with packed fp16 arithmetic, halved and rounded back
-// to e4m3; rotation is linear, so the scales never enter the loop (a rotated
-// pair component is at most sqrt(2) times the pair's largest code, so halving
-// keeps it under 448).  Q codes are rotated in fp32 once per query tile and
-// also multiplied by the mantissa of the score scale 4 s_q s_k c; its power of
-// two is the score MFMA's block scale, and the accumulator starts at -m, so
-// the MFMA returns exp2-domain scores relative to the running max with no
-// per-score VALU work.  P stays bf16 (e4m3 P costs ~2% relative error); V
-// codes are widened exactly to bf16 (every e4m3 value is a bf16 value) and
-// s_v is applied to the output.
+// part of this path, so Q and K are rotated here.  Codes are widened to fp16
+// (exactly), rotated with packed fp16 arithmetic, halved and rounded back to
+// e4m3; rotation is linear, so the scales
+// never enter the loop (a rotated pair component is at most sqrt(2) times the
+// pair's largest code, so halving keeps it under 448).  Scores are fp8 MFMA
+// sums of those codes times 4 * s_q * s_k.  P stays bf16 (e4m3 P costs ~2%
+// relative error); V codes are widened exactly to bf16 (every e4m3 value is a
+// bf16 value) and s_v is applied to the output.
 //
 // Work decomposition, LDS pipeline, softmax and split/merge are those of the
 // bf16 kernel; only the score MFMA (32x32x64 e4m3, K tile in LDS as codes) and
@@ -31,7 +28,6 @@
 namespace flux {
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
@@ -71,20 +67,6 @@ __device__ __forceinline__ uint32_t rope_dword_e4m3(uint32_t x, uint32_t w0, uin
   s16x2 r = __builtin_bit_cast(s16x2, x);  // both halves are overwritten
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, y0, 2.0f, false);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, y1, 2.0f, true);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-// Q codes: one dword (two pairs) rotated in fp32, multiplied by k and halved
-// back to e4m3 (once per query tile, so the exact fp32 form is used).
-__device__ __forceinline__ uint32_t rope_dword_e4m3_scaled(uint32_t x, uint32_t w0, uint32_t w1, float k) {
-  const f32x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)x, 1.0f, false);
-  const f32x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)x, 1.0f, true);
-  float a0, a1, b0, b1;
-  rot_pair(x0[0], x0[1], w0, a0, a1);
-  rot_pair(x1[0], x1[1], w1, b0, b1);
-  s16x2 r = __builtin_bit_cast(s16x2, x);  // both halves are overwritten
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, a0 * k, a1 * k, 2.0f, false);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, b0 * k, b1 * k, 2.0f, true);
   return __builtin_bit_cast(uint32_t, r);
 }
 
@@ -140,20 +122,9 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
   const float s_q = a.scales[(0 * a.batch + b) * H + h];
   const float s_k = a.scales[(1 * a.batch + b) * H + h];
   const float s_v = a.scales[(2 * a.batch + b) * H + h];
-  // Score (exp2 domain) per unit of code dot product, sc = 4 s_q s_k c, split
-  // as sc_frac 2^sc_exp (sc_frac in [0.5, 1)): sc_frac goes into the Q codes
-  // (rotated, times sc_frac, halved), 2^sc_exp into the block scale of the score
-  // MFMA, so the MFMA yields scores in the exp2 domain directly.  (An sc
-  // outside 2^-127 .. 2^127 has its exponent clamped.)
-  int sc_exp;
-  const float sc_frac = frexpf(4.0f * s_q * s_k * a.c, &sc_exp);
-  const int mscale = min(max(sc_exp + 127, 0), 254);  // E8M0 code of 2^sc_exp
-  auto mfma_s = [&](const i32x8& kf, const i32x8& qf, const f32x16& acc) -> f32x16 {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf, acc, 0, 0, 0, mscale, 0, 127);
-  };
+  const float sc = 4.0f * s_q * s_k * a.c;  // score (exp2 domain) per unit of code dot product
 
-  // ---- Q fragments: 32 codes per lane per 64-wide k-step, rotated, scaled by
-  // sc_frac and halved.
+  // ---- Q fragments: 32 codes per lane per 64-wide k-step, rotated and halved.
   const int qrow = qt * C::BM + wave * 32 + l32;
   i32x8 qf[C::KS8];
 #pragma unroll
@@ -171,19 +142,33 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
         cs[0] = rp[0];
         cs[1] = rp[1];
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        y[hf][i] = rope_dword_e4m3_scaled(x[i], cs[i >> 1][2 * (i & 1)], cs[i >> 1][2 * (i & 1) + 1], sc_frac);
+      y[hf] = rope16_e4m3(x, cs);
     }
     const uint32_t w[8] = {y[0][0], y[0][1], y[0][2], y[0][3], y[1][0], y[1][1], y[1][2], y[1][3]};
     qf[t] = __builtin_bit_cast(i32x8, w);
   }
 
   // ---- staging: one 16-code chunk of K and of V per thread and tile.
+  // Thread-to-row maps chosen so that each 16-lane phase of an LDS store
+  // covers every bank once (64 banks of 4 bytes):
+  //   K: a thread stages one 16-code chunk; a phase holds 16 / CPR8 rows
+  //      spaced KSP apart, whose padded rows (D + 16 bytes) then start 64 /
+  //      (16 / CPR8) banks apart.
+  //   V: a thread stages 8 codes of each of two rows (two 8-byte loads) and
+  //      stores each as one 16-byte bf16 chunk; per store a phase covers one
+  //      whole row (D = 128) or two rows 2 apart (D = 64), whose padded rows
+  //      (2 D + 64 bytes) start 32 banks apart.
   const bool st_on = C::NCH >= C::NT || tid < C::NCH;  // every thread stages when D = 128
-  const int st_row = tid / C::CPR8, st_c = tid % C::CPR8;
-  const uint32_t kv_off = (uint32_t)(st_row * tok_stride + st_c * 16);
-  const uint32_t rp_off = (uint32_t)(st_row * (D / 2) * 4 + st_c * 32);
+  const int ph = tid >> 4, pl = tid & 15;  // 16-lane phase, lane in the phase
+  constexpr int KRP = 16 / C::CPR8, KSP = D == 128 ? 8 : 4;
+  const int k_row = (ph % KSP) + KSP * KRP * (ph / KSP) + KSP * (pl / C::CPR8), k_c = pl % C::CPR8;
+  constexpr int VCPR = D / 8, VRP = 16 / VCPR;  // 8-code chunks per row, rows per phase and store
+  const int v_row = 2 * VRP * ph + 2 * (pl / VCPR), v_c = pl % VCPR;  // rows v_row, v_row + 1
+  const uint32_t k_gl = (uint32_t)(k_row * tok_stride + k_c * 16);
+  const uint32_t rp_off = (uint32_t)(k_row * (D / 2) * 4 + k_c * 32);
+  const uint32_t k_lds = (uint32_t)(k_row * C::K8ROW + k_c * 16);
+  const uint32_t v_gl = (uint32_t)(v_row * tok_stride + v_c * 8);
+  const uint32_t v_lds0 = (uint32_t)v_off<D>(v_row, v_c), v_lds1 = (uint32_t)v_off<D>(v_row + 1, v_c);
   u32x4 kraw, vraw;
   u32x4 kcs[2];
   auto stage_load_k = [&](int kt0) {
@@ -193,7 +178,7 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
     const uint32_t rp_bytes = rows > 0 ? (uint32_t)(rows * (D / 2) * 4) : 0u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (size_t)kt0 * tok_stride, kv_bytes);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rope + (size_t)kt0 * (D / 2), rp_bytes);
-    kraw = buffer_load_b128(rk, kv_off);
+    kraw = buffer_load_b128(rk, k_gl);
 #pragma unroll
     for (int i = 0; i < 2; ++i) kcs[i] = buffer_load_b128(rr, rp_off + 16 * i);
   };
@@ -202,13 +187,13 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
     const int rows = N - kt0;
     const uint32_t kv_bytes = rows > 0 ? (uint32_t)((rows - 1) * tok_stride + D) : 0u;
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (size_t)kt0 * tok_stride, kv_bytes);
-    vraw = buffer_load_b128(rv, kv_off);
+    const u32x2 v0 = buffer_load_b64(rv, v_gl), v1 = buffer_load_b64(rv, v_gl + (uint32_t)tok_stride);
+    vraw = (u32x4){v0[0], v0[1], v1[0], v1[1]};
   };
   f32x16 o[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) o[db] = (f32x16){};
-  float m_ref = 0.f;  // reference max (exp2 domain): the score MFMA starts from -m_ref, p = exp2(s)
-  f32x16 fold = {};   // -m_ref in every element: the score accumulator's start
+  float m_ref = 0.f;  // reference of the scaled score (exp2 domain): p = exp2(s * sc - m_ref)
   float lsum = 0.f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int grp = lane >> 4, li = lane & 15;
@@ -223,9 +208,9 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
     i32x8 kf[C::KS8];
 #pragma unroll
     for (int t = 0; t < C::KS8; ++t) kf[t] = kfrag(kl, kb, t);
-    f32x16 s = fold;
+    f32x16 s = {};
 #pragma unroll
-    for (int t = 0; t < C::KS8; ++t) s = mfma_s(kf[t], qf[t], s);
+    for (int t = 0; t < C::KS8; ++t) s = mfma_fp8(kf[t], qf[t], s);
     return s;
   };
   auto mask = [&](int kt0, int kb, f32x16& s) {
@@ -237,22 +222,12 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
   };
   // Reference m as in the bf16 kernel: the first tile of the range sets it to
   // the row max; later tiles form p directly and only move it when a row's
-  // tile sum reaches 2^32 (or is not finite).  s holds score - m_ref.
+  // tile sum reaches 2^32 (or is not finite).
   auto block_max = [&](const f32x16& s) -> float {
     float mt = s[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
-    return fmaxf(mt, swap_halves(mt));
-  };
-  auto rebase = [&](float m_new, f32x16& s) {
-    const float shift = m_ref - m_new;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] += shift;
-  };
-  auto set_ref = [&](float m_new) {
-    m_ref = m_new;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) fold[e] = -m_new;
+    return fmaxf(mt, swap_halves(mt)) * sc;
   };
   auto rescale_o = [&](float alpha) {
     lsum *= alpha;
@@ -261,8 +236,8 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
   };
   auto p_pair = [&](float x0, float x1, float& bsum) -> uint32_t {
     bf16x2 q2;
-    q2[0] = (__bf16)__builtin_amdgcn_exp2f(x0);
-    q2[1] = (__bf16)__builtin_amdgcn_exp2f(x1);
+    q2[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(x0, sc, -m_ref));
+    q2[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(x1, sc, -m_ref));
     bsum = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, bsum, false);
     return __builtin_bit_cast(uint32_t, q2);
   };
@@ -288,15 +263,15 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
   auto store_k = [&](int buf) {
     if (!st_on) return;
     FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
-    lds_write_b128(kl + st_row * C::K8ROW + st_c * 16, rope16_e4m3(kraw, kcs));
+    lds_write_b128(kl + k_lds, rope16_e4m3(kraw, kcs));
   };
   auto store_v = [&](int buf) {
     if (!st_on) return;
     FLUX_LDS char* vl = (FLUX_LDS char*)vsm[buf];
     u32x4 lo, hi;
     e4m3x16_to_bf16(vraw, &lo, &hi);
-    lds_write_b128(vl + v_off<D>(st_row, 2 * st_c), lo);
-    lds_write_b128(vl + v_off<D>(st_row, 2 * st_c + 1), hi);
+    lds_write_b128(vl + v_lds0, lo);
+    lds_write_b128(vl + v_lds1, hi);
   };
 
   // Software pipeline over 64-key tiles, as in the bf16 kernel.  Iteration t:
@@ -313,11 +288,9 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
 
   u32x4 pp[4];  // P(t-1): fragments (block 0, keys 0-15), (0, 16-31), (1, 0-15), (1, 16-31)
   auto rare_move = [&](f32x16& s0, f32x16& s1, float& b) {
-    const float m_new = fmaxf(m_ref, bf16_round(m_ref + fmaxf(block_max(s0), block_max(s1))));
+    const float m_new = fmaxf(m_ref, bf16_round(fmaxf(block_max(s0), block_max(s1))));
     rescale_o(__builtin_amdgcn_exp2f(m_ref - m_new));
-    rebase(m_new, s0);
-    rebase(m_new, s1);
-    set_ref(m_new);
+    m_ref = m_new;
     b = 0.f;
     pp[0] = make_p(s0, 0, b);
     pp[1] = make_p(s0, 1, b);
@@ -335,12 +308,7 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
       mask(kt0, 0, s0);
       mask(kt0, 1, s1);
     }
-    {
-      const float m_new = bf16_round(m_ref + fmaxf(block_max(s0), block_max(s1)));
-      rebase(m_new, s0);
-      rebase(m_new, s1);
-      set_ref(m_new);
-    }
+    m_ref = bf16_round(fmaxf(block_max(s0), block_max(s1)));
     float b = 0.f;
     pp[0] = make_p(s0, 0, b);
     pp[1] = make_p(s0, 1, b);
@@ -380,7 +348,7 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
     FLUX_LDS char* kw = (FLUX_LDS char*)ksm[(i + 1) & 1];  // K(t+1)
     FLUX_LDS char* vw = (FLUX_LDS char*)vsm[i & 1];        // V(t)
     u32x4 ky, vlo, vhi;
-    f32x16 s0 = fold, s1 = fold;
+    f32x16 s0 = (f32x16){}, s1 = (f32x16){};
     float b = 0.f;
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, NL>([&](auto jc) {
@@ -388,8 +356,8 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
       if constexpr (j < NK) {
         const i32x8 x = fk[j % 2];
         if constexpr (j + 2 < NK) fk[j % 2] = kfrag(kl, (j + 2) / C::KS8, (j + 2) % C::KS8);
-        if constexpr (j < C::KS8) s0 = mfma_s(x, qf[j], s0);
-        else s1 = mfma_s(x, qf[j - C::KS8], s1);
+        if constexpr (j < C::KS8) s0 = mfma_fp8(x, qf[j], s0);
+        else s1 = mfma_fp8(x, qf[j - C::KS8], s1);
       } else {
         constexpr int v = j - NK, q4 = v / C::DB, db = v % C::DB;
         const u32x4 x = fv[v % NPF];
@@ -412,15 +380,15 @@ __device__ __forceinline__ void fp8_tile(const Fp8Args& a, char (&ksm)[2][Fp8Cfg
       if constexpr (j >= R0 && j < R0 + RS) {
         if (st_on) ky[j - R0] = rope_dword_e4m3(kraw[j - R0], kcs[(j - R0) >> 1][2 * ((j - R0) & 1)], kcs[(j - R0) >> 1][2 * ((j - R0) & 1) + 1]);
         if constexpr (j == R0 + RS - 1) {
-          if (st_on) lds_write_b128(kw + st_row * C::K8ROW + st_c * 16, ky);
+          if (st_on) lds_write_b128(kw + k_lds, ky);
         }
       }
       constexpr int RV = NK > R0 + RS ? NK : R0 + RS;  // V(t) staging slot
       if constexpr (j == RV) {
         if (st_on) {
           e4m3x16_to_bf16(vraw, &vlo, &vhi);
-          lds_write_b128(vw + v_off<D>(st_row, 2 * st_c), vlo);
-          lds_write_b128(vw + v_off<D>(st_row, 2 * st_c + 1), vhi);
+          lds_write_b128(vw + v_lds0, vlo);
+          lds_write_b128(vw + v_lds1, vhi);
         }
       }
       if constexpr (j == RV + 1) stage_load_k((t + 2) * C::BN);

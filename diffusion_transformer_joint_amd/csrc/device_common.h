@@ -75,6 +75,10 @@ __device__ __forceinline__ u32x4 buffer_load_b128(__amdgpu_buffer_rsrc_t r, uint
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
 }
 
+__device__ __forceinline__ u32x2 buffer_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voffset, 0, 0));
+}
+
 __device__ __forceinline__ uint32_t buffer_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t voffset) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voffset, 0, 0));
 }
