@@ -18,6 +18,8 @@ Extra fields of the same JSON line (each with its own timing):
     two references, the 66,048-token e4m3 call;
   * one GPU's share of the edit call when its heads are split over 8, 4 or 2
     GPUs (3, 6 and 12 heads);
+  * the 3-head share and the edit call captured once into a HIP graph and
+    replayed (one graph launch per call instead of three kernel launches);
   * the edit call in segment-local mode, with cold caches, its backward, and
     tile-sparse attention on edit-call tokens with position-local attention.
 Per workload: seed, SHA-256 of the input bytes, attention-kernel time (mean of
@@ -152,6 +154,42 @@ def measure(w, steps, warmup, mode="joint", keep_output=False):
         r["frac_mixed_ceiling"] = r["kernel_tflops"] / MIXED_CEIL
     output = out.view(torch.int16).cpu().numpy().view(np.uint16) if keep_output else None
     return r, inp, output
+
+
+def measure_graph(w, steps, warmup):
+    """The joint call captured once into a HIP graph (RoPE table, attention,
+    merge) and replayed: `warmup` untimed replays, then `steps` timed ones
+    (events on the replay stream).  Launch work per call is one graph launch."""
+    import torch
+    from diffusion_transformer_joint_amd import inputs as I
+    from diffusion_transformer_joint_amd.flux_attn import Plan
+
+    inp = I.make_inputs(w)
+    q, k, v, pos, sc = _device_inputs(inp)
+    out = torch.empty((w.batch, w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda:0")
+    plan = Plan(w.batch, w.heads, w.head_dim, w.tokens, dtype="fp8" if w.fp8 else "bf16")
+    plan.forward(q, k, v, w.segment_tokens, pos, out=out, scales=sc)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.forward(q, k, v, w.segment_tokens, pos, out=out, scales=sc)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    del g
+    plan.close()
+    return {"workload": f"{w.name} (one call captured in a HIP graph, replayed)", "tokens": w.tokens,
+            "heads": w.heads, "head_dim": w.head_dim, "batch": w.batch, "dtype": "fp8_e4m3" if w.fp8 else "bf16",
+            "flops": w.flops(), "steps": steps, "warmup": warmup, "ms_per_step": step_ms,
+            "tflops": w.flops() / (step_ms * 1e-3) / 1e12}
 
 
 def measure_cold(w, calls, flush_mib=512):
@@ -432,6 +470,10 @@ def main():
             extra.append(r)
             log(f"{r['workload']}: {r['kernel_tflops']:.1f} TFLOP/s kernel ({r['frac_bf16_peak']:.3f} of bf16 peak), "
                 f"clock {r['clock_mhz']:.0f} MHz")
+        for w, k_, w_ in ((share(3), min(K, 200), min(W, 400)), (WL["edit1024"], min(K, 100), min(W, 200))):
+            r = measure_graph(w, k_, w_)
+            extra.append(r)
+            log(f"{r['workload']}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['tflops']:.1f} TFLOP/s per step")
         r = measure_cold(WL["edit1024"], max(5, min(K, 20)))
         extra.append(r)
         log(f"{r['workload']}: {r['kernel_tflops_median']:.1f} TFLOP/s kernel (median)")

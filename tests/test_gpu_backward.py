@@ -25,6 +25,8 @@ plus the angle term e = (2^-12 + 2^-22)(|x0| + |x1|) per pair component
 so every score moves by at most sum_d (da |b_d| + |a_d| db + da db) with
 da = 2^-9 (|a_d| + e_d) + e_d, and the log-sum-exp, 1-Lipschitz in the
 largest score change, by at most ln 2 times that; plus the 2.5e-3 of (1).
+(3) The mean of (1) over a case's rows must stay under 2e-3: the worst-row
+bounds are loose by design, the mean catches a systematic error.
 """
 import numpy as np
 import pytest
@@ -131,9 +133,16 @@ def test_backward_against_oracle(name, batch, heads, d, segs, sigma):
     lerr_b = np.abs(lse - lb)
     lerr = np.abs(lse - rl)
     say(f"  {name}: lse max-abs vs rounded operands {lerr_b.max():.2e} (bound {float(lflip.max()) + 2.5e-3:.2e}), "
-        f"vs exact {lerr.max():.2e} (bound {float(lbound.max()) + 2.5e-3:.2e})")
+        f"mean {lerr_b.mean():.2e}, 99th percentile {np.quantile(lerr_b, 0.99):.2e}; "
+        f"vs exact {lerr.max():.2e} (bound {float(lbound.max()) + 2.5e-3:.2e}), mean {lerr.mean():.2e}")
     assert np.all(lerr_b <= lflip + 2.5e-3)
     assert np.all(lerr <= lbound + 2.5e-3)
+    # The per-row bounds above hold for the worst row.  On the rows of a
+    # case together the error is the rounding noise of l (bf16 p, 2^-9 each,
+    # independent signs) and of rare one-ulp operand flips, so its mean sits
+    # far below them (measured 4e-5 to 7.2e-4 over these cases); a systematic
+    # lse error of 2e-3 or more (a wrong base, offset or missing term) fails here.
+    assert lerr_b.mean() <= 2e-3, f"{name}: mean lse error {lerr_b.mean():.2e}"
     for gname, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         ma, rel = errors(got, ref)
         say(f"  {name} {gname}: max-abs {ma:.3e} rel-L2 {rel:.3e} (|ref| max {np.abs(ref).max():.3e})")
