@@ -99,17 +99,34 @@ __global__ __launch_bounds__(256) void block_select_kernel(const float* __restri
 // its query tile, each query keeping its largest score L, then every key tile
 // t, each wave reducing max over its queries of (tile max - L) into
 // red[wave][t]; at the end red's column maxima decide the mask row.  K tiles
-// are double-buffered in LDS, one barrier per tile.
+// are double-buffered in LDS, one barrier per tile.  Keys past N are masked
+// in the one tile that holds them only; the per-query values of 32 tiles
+// are collected in LDS (one store per tile) and each lane then reduces one
+// tile's 32 values, instead of a shuffle reduction per tile.
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void tile_bound_kernel(BoundArgs a) {
   constexpr int BN = 64, NT = 512, KSTEPS = D / 16, CPR = D / 8, RPP = NT / CPR, NPASS = BN / RPP;
   constexpr int KTILEB = BN * LdsRows<D>::K;
   __shared__ __attribute__((aligned(16))) char ksm[2][KTILEB];
+  __shared__ __attribute__((aligned(16))) float vbuf[8][32][32];  // [wave][tile % 32][query]
   extern __shared__ float red[];  // [8][KT]
   const int N = a.n_tokens, H = a.heads, KT = a.kt;
   const int QT = (N + 255) / 256;
-  const int qt = blockIdx.x % QT, bh = blockIdx.x / QT;
+  // Work item: a whole query tile, or one piece (a range of key tiles) of a
+  // query tile of the last round; the mask bits of a key tile depend only on
+  // that tile and the aligned ones, so pieces need no merge.
+  int tile, kt_lo = 0, kt_hi = KT;
+  if ((int)blockIdx.x < a.whole) {
+    tile = xcd_tile_order(blockIdx.x, a.whole);
+  } else {
+    const int slot = blockIdx.x - a.whole;
+    tile = a.whole + slot / a.split;
+    const int piece = slot % a.split;
+    kt_lo = piece * KT / a.split;
+    kt_hi = (piece + 1) * KT / a.split;
+  }
+  const int qt = tile % QT, bh = tile / QT;
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -131,10 +148,11 @@ void tile_bound_kernel(BoundArgs a) {
     qf[t] = __builtin_bit_cast(bf16x8, rope_chunk_scaled(x, w, a.c));
   }
 
-  // key tile of position p: the 4 aligned tiles first, then all KT
+  // key tile of position p: the 4 aligned tiles first, then kt_lo .. kt_hi - 1
   const int t_al0 = 4 * qt, n_al = min(4, KT - t_al0);
-  auto tile_of = [&](int p) { return p < n_al ? t_al0 + p : p - n_al; };
-  const int n_pos = n_al + KT;
+  auto tile_of = [&](int p) { return p < n_al ? t_al0 + p : kt_lo + p - n_al; };
+  const int n_rng = kt_hi - kt_lo;
+  const int n_pos = n_al + n_rng;
   const int st_chunk = tid % CPR, st_row0 = tid / CPR;
   u32x4 kraw[NPASS], kcs[NPASS];
   auto load_k = [&](int kt0) {
@@ -156,44 +174,99 @@ void tile_bound_kernel(BoundArgs a) {
     for (int p = 0; p < NPASS; ++p)
       lds_write_b128(kl + k_off<D>(st_row0 + p * RPP, st_chunk), rope_chunk(kraw[p], kcs[p]));
   };
+  auto store_rotated = [&](int buf, const u32x4 (&kr)[NPASS]) {
+    FLUX_LDS char* kl = (FLUX_LDS char*)ksm[buf];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) lds_write_b128(kl + k_off<D>(st_row0 + p * RPP, st_chunk), kr[p]);
+  };
 
   load_k(tile_of(0) * BN);
   store_k(0);
   if (n_pos > 1) load_k(tile_of(1) * BN);
   __syncthreads();
   float low = -INFINITY;  // L of this lane's query
+  // Lane j < n of the wave: the maximum over the wave's 32 queries of the
+  // values stored for range tile t0 + j (slot j of vbuf) goes to
+  // red[wave][kt_lo + t0 + j].
+  auto flush = [&](int t0, int n) {
+    if (lane < n) {
+      const float* row = &vbuf[wave][lane][0];
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const float4 x = *(const float4*)(row + i);
+        m = fmaxf(m, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+      }
+      red[wave * KT + kt_lo + t0 + lane] = m;
+    }
+  };
   for (int p = 0; p < n_pos; ++p) {
     const int t = tile_of(p), kt0 = t * BN;
     const FLUX_LDS char* kl = (const FLUX_LDS char*)ksm[p & 1];
+    // the previous 32 tiles' values were stored before the last barrier
+    if (p > n_al && ((p - n_al) & 31) == 0) flush(p - n_al - 32, 32);
+    // The score MFMAs of this tile in a fixed order, each with the LDS read
+    // of the K fragment two MFMAs ahead and, in every other slot, the
+    // rotation of one pair of the next K tile (loaded one iteration ahead).
+    constexpr int NM = 2 * KSTEPS, NPAIR = NPASS * 4;
+    static_assert(2 * NPAIR <= NM, "one rotated pair per two MFMAs");
+    auto kfrag = [&](int j) {
+      return __builtin_bit_cast(bf16x8, lds_read_b128(kl + k_off<D>(32 * (j / KSTEPS) + l32, 2 * (j % KSTEPS) + g)));
+    };
+    f32x16 s[2] = {(f32x16){}, (f32x16){}};
+    u32x4 kr[NPASS];
+    bf16x8 fk[2] = {kfrag(0), kfrag(1)};
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const bf16x8 x = fk[j % 2];
+      if constexpr (j + 2 < NM) fk[j % 2] = kfrag(j + 2);
+      s[j / KSTEPS] = mfma_bf16(x, qf[j % KSTEPS], s[j / KSTEPS]);
+      if constexpr (j % 2 == 0 && j / 2 < NPAIR) {
+        constexpr int pi = j / 2;
+        kr[pi / 4][pi % 4] = rope_pair(kraw[pi / 4][pi % 4], kcs[pi / 4][pi % 4]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // The other buffer was last read in the previous tile, before the
+    // barrier; after the last tile nothing reads it, so the store is
+    // unconditional.
+    store_rotated((p + 1) & 1, kr);
     float mx = -INFINITY;
+    if (kt0 + BN <= N) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = {};
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int tt = 0; tt < KSTEPS; ++tt)
-        s = mfma_bf16(__builtin_bit_cast(bf16x8, lds_read_b128(kl + k_off<D>(32 * kb + l32, 2 * tt + g))), qf[tt], s);
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    } else {
       // element e of lane l: key 32 kb + 8 (e / 4) + 4 g + e % 4 of the tile
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kt0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-        mx = fmaxf(mx, key < N ? s[e] : -INFINITY);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+          mx = fmaxf(mx, key < N ? s[kb][e] : -INFINITY);
+        }
     }
     mx = fmaxf(mx, swap_halves(mx));  // this query's largest score over the tile
-    if (p + 1 < n_pos) store_k((p + 1) & 1);
     if (p < n_al) {
       low = fmaxf(low, mx);
-    } else {
-      float v = qrow < N ? mx - low : -INFINITY;
-#pragma unroll
-      for (int off = 16; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-      if (lane == 0) red[wave * KT + t] = v;
+    } else if (g == 0) {
+      vbuf[wave][(p - n_al) & 31][l32] = qrow < N ? mx - low : -INFINITY;
     }
     if (p + 2 < n_pos) load_k(tile_of(p + 2) * BN);
     __syncthreads();
   }
-  uint8_t* mrow = a.mask + (size_t)blockIdx.x * KT;
-  for (int t = tid; t < KT; t += NT) {
+  {
+    const int done = n_rng & ~31;  // range tiles already reduced into red
+    if (done < n_rng) flush(done, n_rng - done);
+    else if (n_rng > 0) flush(n_rng - 32, 32);
+  }
+  __syncthreads();
+  uint8_t* mrow = a.mask + (size_t)tile * KT;
+  for (int t = kt_lo + tid; t < kt_hi; t += NT) {
     float m = red[t];
 #pragma unroll
     for (int w = 1; w < 8; ++w) m = fmaxf(m, red[w * KT + t]);
@@ -318,9 +391,22 @@ hipError_t launch_block_select(const float* qbar, const float* kbar, uint8_t* ma
   return hipGetLastError();
 }
 
-hipError_t launch_tile_bound(const BoundArgs& a, int head_dim, hipStream_t stream) {
+hipError_t launch_tile_bound(const BoundArgs& args, int head_dim, int num_cus, hipStream_t stream) {
+  BoundArgs a = args;
   const int QT = (a.n_tokens + 255) / 256;
-  const dim3 grid((unsigned)(a.batch * a.heads * QT));
+  const int tiles = a.batch * a.heads * QT;
+  // Full rounds of whole query tiles; the tiles of a partial last round are
+  // cut into key-tile ranges (at most 8 pieces, at least 8 key tiles each) so
+  // that the round fills the compute units.
+  const int C = num_cus > 0 ? num_cus : 1;
+  const int rest = tiles % C;
+  int split = rest > 0 ? C / rest : 1;
+  split = split < 8 ? split : 8;
+  split = split < a.kt / 8 ? split : a.kt / 8;
+  if (split < 2) split = 1;
+  a.whole = split > 1 ? tiles - rest : tiles;
+  a.split = split;
+  const dim3 grid((unsigned)(a.whole + (tiles - a.whole) * split));
   const size_t lds = (size_t)8 * a.kt * sizeof(float);
   if (lds > kBoundMaxLds) return hipErrorInvalidValue;
   if (head_dim == 128)

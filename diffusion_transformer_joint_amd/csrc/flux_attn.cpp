@@ -754,7 +754,7 @@ int flux_attn_block_mask(flux_attn_plan* plan, const void* q, const void* k, con
   a.kt = KT;
   a.c = plan_c(c);
   a.log2_tau = std::log2(tau);
-  e = flux::launch_tile_bound(a, c.head_dim, stream);
+  e = flux::launch_tile_bound(a, c.head_dim, plan->num_cus, stream);
   if (e != hipSuccess) return hip_fail(e, "block mask launch");
   return ok();
 }

@@ -156,10 +156,12 @@ struct BoundArgs {
   int kt;                 // ceil(N / 64)
   float c;                // scale * log2(e)
   float log2_tau;
+  int whole;              // set by launch_tile_bound: query tiles run over all key tiles,
+  int split;              // and pieces per remaining query tile (key-tile ranges)
 };
 // Dynamic LDS of the per-wave reductions (8 x KT floats): KT <= 2048.
 constexpr size_t kBoundMaxLds = 64 * 1024;
-hipError_t launch_tile_bound(const BoundArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_tile_bound(const BoundArgs& a, int head_dim, int num_cus, hipStream_t stream);
 // Kept key tiles of each mask row (ascending) into list[row * stride + i], count[row].
 hipError_t launch_mask_to_list(const uint8_t* mask, int* list, int* count, int rows, int KT, int stride,
                                hipStream_t stream);

@@ -108,8 +108,19 @@ def test_edit1024_local_oracle_mask_sampled_rows():
 
 
 def _mask_workload(name):
-    if name == "sp_small":
-        w = custom("sp_small", 3, 128, [S("text", 200), S("image", 30, 30)], sigma=1.5)
+    small = {
+        # 1,100 tokens: 18 key tiles, the last one ragged
+        "sp_small": (3, 128, [S("text", 200), S("image", 30, 30)], 1),
+        # 2,000 tokens: exactly 32 key tiles (one full group of the kernel's
+        # per-32-tile reduction), the last one ragged
+        "sp_kt32": (2, 128, [S("text", 80), S("image", 40, 48)], 1),
+        # head_dim 64, batch 2, 4,166 tokens: 66 key tiles (two full groups + 2),
+        # the last one ragged
+        "sp_d64_b2": (2, 64, [S("text", 70), S("image", 64, 64)], 2),
+    }
+    if name in small:
+        heads, d, segs, batch = small[name]
+        w = custom(name, heads, d, segs, batch=batch, sigma=1.5)
         return I.Workload(w.name, w.batch, w.heads, w.head_dim, w.segments, w.sigma, w.fp8, w.seed,
                           w.description, 0.9)
     return I.WORKLOADS[name]
@@ -135,7 +146,7 @@ def test_pooled_mask_matches_oracle_rule(name, tau):
 
 
 @pytest.mark.parametrize("name,tau", [("edit1024_local", 0.1), ("edit1024_local", 0.01), ("sp_small", 0.3),
-                                      ("sp_small", 0.03)])
+                                      ("sp_small", 0.03), ("sp_kt32", 0.1), ("sp_d64_b2", 0.1)])
 def test_bound_mask_matches_oracle_rule(name, tau):
     import time
     import torch
