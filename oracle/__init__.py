@@ -10,8 +10,10 @@ What it computes (every function cites the passage it follows):
   * ``rope``       - multi-axis rotary position embedding in fp64;
   * ``softmax_attention`` - non-causal softmax attention over the whole joint sequence,
                      blocked over query rows, fp64;
-  * ``e4m3``       - decoding of OCP 8-bit e4m3 ("e4m3fn") codes from the
-                     format's definition;
+  * ``e4m3``       - decoding of OCP 8-bit e4m3 ("e4m3fn") codes and
+                     nearest-even rounding to them, from the format's definition;
+  * ``fp8_requant`` - attention of the FP8 path with its second quantization
+                     (rotated Q and K rounded to e4m3 again);
   * ``block_sparse`` - the tile-mask rules of threshold-sparse attention (the
                      score-bound rule with its error bound against dense
                      attention, and the pooled-score rule) and exact
@@ -28,7 +30,8 @@ from .rope import rope_frequencies, rope_angles, apply_rope  # noqa: F401
 from .softmax_attention import (softmax_rows, attention_from_scores, attention,  # noqa: F401
                         joint_rope_attention, joint_rope_attention_rows,
                         segment_local_rope_attention)
-from .e4m3 import e4m3_decode, e4m3_table, dequantize  # noqa: F401
+from .e4m3 import e4m3_decode, e4m3_table, dequantize, e4m3_round  # noqa: F401
+from .fp8_requant import requantized_operands, fp8_requant_attention  # noqa: F401
 from .inputs_fp64 import inputs_to_fp64  # noqa: F401
 from .block_sparse import (tile_means, block_scores, block_mask, block_sparse_attention,  # noqa: F401
                            tile_score_maxima, bound_mask, skipped_mass, skip_mass_bound, dense_error_bound)

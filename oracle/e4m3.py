@@ -31,3 +31,25 @@ def dequantize(codes, scales):
     """codes [B,N,H,D] uint8, scales [B,H] -> fp64 values codes * scale per (b,h)."""
     vals = e4m3_table()[np.asarray(codes, dtype=np.uint8)]
     return vals * np.asarray(scales, dtype=np.float64)[:, None, :, None]
+
+
+def e4m3_round(x):
+    """Round fp64 values to the nearest e4m3 value (ties to the even code, that
+    is the one whose mantissa's last bit is 0), saturating at +-448 (the
+    e4m3fn conversion with saturation: there is no infinity to round to).
+
+    Written from the format: the finite non-negative values in code order are
+    increasing, so the nearest one is found by a search over that sorted list.
+    Returns fp64 values (the decoded rounded codes); NaN stays NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    pos = e4m3_table()[:127]                      # codes 0x00..0x7E: 0 .. 448, increasing
+    a = np.minimum(np.abs(x), pos[-1])
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 1, len(pos) - 1)
+    lo = hi - 1
+    d_lo, d_hi = a - pos[lo], pos[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    r = np.where(take_hi, pos[hi], pos[lo])
+    r = np.where(a == pos[hi], pos[hi], r)
+    return np.where(np.isnan(x), np.nan, np.copysign(r, x))
+

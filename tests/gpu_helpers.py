@@ -8,6 +8,10 @@ from diffusion_transformer_joint_amd import inputs as I
 
 BF16_TOL = (2e-2, 5e-3)   # (max-abs, relative L2) against the fp64 oracle
 FP8_TOL = (6e-2, 2e-2)
+# e4m3 kernel against oracle.fp8_requant_attention (the same requantization in
+# fp64): what is left is bf16 P, the fp16 rotation (an e4m3 rounding decision
+# within 2^-11 of a midpoint may go the other way) and fp32 sums
+FP8_REQUANT_TOL = (6e-2, 1e-2)
 
 
 def say(*a):

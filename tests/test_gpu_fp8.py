@@ -11,7 +11,8 @@ import pytest
 import oracle
 from diffusion_transformer_joint_amd import inputs as I
 
-from gpu_helpers import FP8_TOL, assert_close, custom, out_fp64, ref_full, ref_rows, run_hip, sample_rows, say
+from gpu_helpers import (FP8_REQUANT_TOL, FP8_TOL, assert_close, custom, errors, out_fp64, ref_full, ref_rows,
+                         run_hip, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,3 +91,28 @@ def test_fp8_scales_apply_per_head():
     sc[2] *= np.array([[2.0, 0.25, 1.0]], np.float32)
     inp = dataclasses.replace(inp, scales=sc)
     assert_close(out_fp64(run_hip(inp)), ref_full(inp), FP8_TOL, "per-head scales")
+
+
+REQUANT_CASES = [
+    ("rq_sigma1_n1000", 1, 3, 128, [S("text", 40), S("image", 24, 40)], 1.0, "joint"),
+    ("rq_sigma1_d64_local", 1, 3, 64, [S("image", 36, 8)], 1.0, "segment_local"),
+    ("rq_sigma05_b2", 2, 2, 128, [S("text", 45), S("image", 12, 24)], 0.5, "joint"),
+]
+
+
+@pytest.mark.parametrize("name,batch,heads,d,segs,sigma,mode", REQUANT_CASES, ids=[c[0] for c in REQUANT_CASES])
+def test_fp8_against_requantized_oracle(name, batch, heads, d, segs, sigma, mode):
+    # The path rounds the rotated Q and K to e4m3 a second time (reading of
+    # where FP8 quantization sits); oracle.fp8_requant_attention is that
+    # arithmetic in fp64.  The plain oracle's distance is reported: at sigma 1
+    # the requantization alone moves the result by ~2.5% (beyond 2e-2).
+    inp = I.make_inputs(custom(name, heads, d, segs, batch=batch, sigma=sigma, fp8=True, seed=41))
+    got = out_fp64(run_hip(inp, mode=mode))
+    rq = oracle.fp8_requant_attention(inp.q, inp.k, inp.v, inp.scales, inp.pos, inp.workload.axes_dim,
+                                      segment_tokens=inp.segment_tokens if mode == "segment_local" else None)
+    assert_close(got, rq, FP8_REQUANT_TOL, f"{name} vs requantized-operand oracle")
+    ma, rl = errors(got, ref_full(inp, mode=mode))
+    ma2, rl2 = errors(rq, ref_full(inp, mode=mode))
+    say(f"  {name}: plain oracle vs kernel rel-L2 {rl:.3e}, vs requantized oracle {rl2:.3e}")
+    # the kernel's distance from the plain oracle is the requantization's, give or take the rest
+    assert abs(rl - rl2) <= 0.25 * rl2 + 2e-3
