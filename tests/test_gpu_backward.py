@@ -118,6 +118,25 @@ CASES = [
 ]
 
 
+def _random_cases(n=10, seed=77):
+    """Seeded random shapes: batch 1-2, 1-3 heads, head_dim 64/128, an optional
+    text segment and an image grid (N from 1 to ~1,500), sigma 0.5 or 1."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        segs = []
+        nt = int(rng.choice([0, 1, int(rng.integers(2, 400))]))
+        if nt:
+            segs.append(S("text", nt))
+        segs.append(S("image", int(rng.integers(1, 34)), int(rng.integers(1, 34))))
+        out.append((f"bw_rnd{i:02d}", int(rng.choice([1, 1, 2])), int(rng.integers(1, 4)), int(rng.choice([64, 128])),
+                    segs, float(rng.choice([0.5, 1.0]))))
+    return out
+
+
+CASES = CASES + _random_cases()
+
+
 @pytest.mark.parametrize("name,batch,heads,d,segs,sigma", CASES, ids=[c[0] for c in CASES])
 def test_backward_against_oracle(name, batch, heads, d, segs, sigma):
     inp = I.make_inputs(custom(name, heads, d, segs, batch=batch, sigma=sigma))
